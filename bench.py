@@ -1,0 +1,194 @@
+"""Benchmark of the fine-grained FP8 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+
+Workload: the dense Fprop at real width -- X[4096 x 7168] bf16 ~N(0,1) with
+0.1% x100 outliers, W[18432 x 7168] bf16 ~N(0,0.02).  One step is the whole
+hot path over that batch, inputs already in HBM:
+    quantise X in 1x128 tiles  (fp8_quant_tile, FP32 scales)
+    quantise W in 128x128 blocks (fp8_quant_block, FP32 scales)
+    Y = X W^T, block-scaled FP8 GEMM with per-128 FP32 promotion, bf16 out.
+
+Prints one JSON line.  `value` is the step's GEMM FLOPs over the step time
+(quantisation included); `roofline` covers the dominant kernel (the GEMM),
+its duration measured with HIP events on the stream it runs on;
+`quantizers` gives each quantiser's GB/s against HBM; `cpu_baseline` is the
+CPU oracle on a bounded sub-block of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, N, K = 4096, 18432, 7168
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_fprop_traffic.json")
+KERNEL_SOURCES = ["block_scaled_gemm_amd/csrc/gemm.hip", "block_scaled_gemm_amd/csrc/device.h"]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def quant_bytes_row(rows, cols):
+    """Algorithmic bytes of 1x128 quantisation: 2 B in, 1 B out per
+    element, 4 B per group."""
+    return rows * cols * 3 + rows * (cols // 128) * 4
+
+
+def quant_bytes_block(rows, cols):
+    return rows * cols * 3 + ((rows + 127) // 128) * (cols // 128) * 4
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(X, W, target_s=10.0):
+    """Time the CPU oracle on a sub-block of the workload: quantise X rows
+    [0, ms) and W rows [0, ns), then their GEMM; grow ns until the run takes
+    about target_s.  Returns the baseline dict."""
+    import oracle
+    orc = oracle.default()
+    ms, ns = 128, 256
+    while True:
+        x, w = X[:ms], W[:ns]
+        t0 = time.perf_counter()
+        qx, sx = orc.quant_tile(x, 0, 0)
+        qw, sw, _ = orc.quant_block(w, 0)
+        orc.gemm(qx, sx, qw, sw, 0, sw.shape[1], 1)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or ns >= N:
+            break
+        ns = min(N, ns * max(2, int(target_s / max(dt, 1e-3))))
+        ns = (ns + 127) // 128 * 128
+    flops = 2.0 * ms * ns * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"X rows 0..{ms - 1} x W rows 0..{ns - 1} of the same workload "
+                      f"(quant 1x128 + quant 128x128 + GEMM {ms}x{ns}x{K}), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "
+              "single-GPU build (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_gemm_amd as bs
+    from block_scaled_gemm_amd import inputs
+
+    t_gen = time.perf_counter()
+    d = inputs.dense_fprop()
+    Xh, Wh = d["X"], d["W"]
+    dev = torch.device("cuda:0")
+    X = torch.from_numpy(Xh.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(Wh.view(np.int16)).to(dev).view(torch.bfloat16)
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_FP32, q=qx, s=sx)
+        if ev is not None:
+            ev[1].record()
+        bs.fp8_quant_block(W, bs.SCALE_FP32, q=qw, s=sw)
+        if ev is not None:
+            ev[2].record()
+        bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    qx_ms = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    qw_ms = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    gemm_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = wall * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps: {step_ms:.3f} ms/step (quant X {qx_ms:.3f}, quant W {qw_ms:.3f}, "
+          f"gemm {gemm_ms:.3f} ms)", file=sys.stderr, flush=True)
+
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    bx, bw = quant_bytes_row(M, K), quant_bytes_block(N, K)
+    traffic = measured_traffic()
+    out = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% MFMA peak); quantize GB/s (% HBM peak)",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded numpy: N(0,1) with 0.1% x100 outliers; N(0,0.02))",
+        "config": {"workload": "dense Fprop: quant X[4096x7168] 1x128 + quant W[18432x7168] 128x128 "
+                               "+ GEMM 4096x18432x7168 -> bf16",
+                   "M": M, "N": N, "K": K, "scales": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_FP8_TFLOPS,
+                     "traffic": traffic, "kernel": "gemm_kernel<0,0,false>",
+                     "kernel_ms": gemm_ms},
+        "quantizers": {
+            "quant_tile_row_X": {"ms": qx_ms, "GB/s": bx / (qx_ms * 1e-3) / 1e9,
+                                 "frac_hbm": bx / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+            "quant_block_W": {"ms": qw_ms, "GB/s": bw / (qw_ms * 1e-3) / 1e9,
+                              "frac_hbm": bw / (qw_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sub-block", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(Xh, Wh)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

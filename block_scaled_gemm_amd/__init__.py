@@ -1,0 +1,225 @@
+"""Python binding of libfp8bs.so: fine-grained FP8 quantisation and the
+block-scaled FP8 GEMM on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libfp8bs.so.  PyTorch provides device memory and the current stream.  There
+is no fallback: if the library is missing, every call raises.
+
+Functions carry the C names (see include/fp8bs.h for the full contract):
+
+    fp8_cast_e4m3(x)                                -> q
+    fp8_quant_tile(x, axis, scale_mode)             -> (q, s)
+    fp8_quant_block(w, scale_mode, transpose=False) -> (q, s, qt)
+    fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype) -> d
+    fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype, rows_bound=None)    -> d
+
+bf16 inputs are ``torch.bfloat16`` tensors (their bit patterns are what the
+library reads); codes are ``torch.uint8``; scales ``torch.float32``.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8bs.so")
+
+AXIS_ROW, AXIS_COL = 0, 1
+SCALE_FP32, SCALE_POW2 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+BSCALE_BLOCK, BSCALE_TILE = 0, 1
+
+_lib = None
+
+
+class FP8BSError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+def lib():
+    """The loaded libfp8bs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m block_scaled_gemm_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.fp8bs_abi_version.restype = i32
+        L.fp8bs_abi_version.argtypes = []
+        L.fp8bs_status_string.restype = ctypes.c_char_p
+        L.fp8bs_status_string.argtypes = [i32]
+        L.fp8_cast_e4m3.restype = i32
+        L.fp8_cast_e4m3.argtypes = [vp, i64, vp, vp]
+        L.fp8_quant_tile.restype = i32
+        L.fp8_quant_tile.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp]
+        L.fp8_quant_block.restype = i32
+        L.fp8_quant_block.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
+        L.fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8_gemm_blockscaled.restype = i32
+        L.fp8_gemm_blockscaled.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32,
+                                           i64, i64, vp, i64, i32, vp, ctypes.c_size_t, vp]
+        L.fp8_grouped_gemm.restype = i32
+        L.fp8_grouped_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp, vp,
+                                       i64, i32, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().fp8bs_status_string(int(status)).decode()
+
+
+def abi_version():
+    return lib().fp8bs_abi_version()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise FP8BSError(rc, what)
+
+
+def _dev(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() >= 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+
+
+def _ld(t):
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+# ---- quantisation ------------------------------------------------------------------
+
+def fp8_cast_e4m3(x):
+    """E4M3 codes of an fp32 tensor (nearest, ties to even, saturating)."""
+    _dev(x, "x", torch.float32)
+    x = x.contiguous()
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_cast_e4m3(_ptr(x), x.numel(), _ptr(q), _stream()), "fp8_cast_e4m3")
+    return q
+
+
+def fp8_quant_tile(x, axis=AXIS_ROW, scale_mode=SCALE_FP32, q=None, s=None):
+    """1x128 (axis ROW) or 128x1 (axis COL) group quantisation of bf16 x
+    [rows, cols].  ROW: q [rows, cols], s [cols/128, rows].  COL: q [cols,
+    rows] (transposed), s [rows/128, cols]."""
+    _dev(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    if axis == AXIS_ROW:
+        qs, ss = (rows, cols), (cols // 128, rows)
+    else:
+        qs, ss = (cols, rows), (rows // 128, cols)
+    if q is None:
+        q = torch.empty(qs, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(ss, dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quant_tile(_ptr(x), rows, cols, _ld(x), int(axis), int(scale_mode),
+                                _ptr(q), _ld(q), _ptr(s), _ld(s), _stream()), "fp8_quant_tile")
+    return q, s
+
+
+def fp8_quant_block(w, scale_mode=SCALE_FP32, transpose=False, q=None, s=None, qt=None):
+    """128x128 block quantisation of bf16 w [rows, cols]: q [rows, cols],
+    s [ceil(rows/128), cols/128] and, with transpose=True, qt [cols, rows]."""
+    _dev(w, "w", torch.bfloat16)
+    rows, cols = w.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty(((rows + 127) // 128, cols // 128), dtype=torch.float32, device=w.device)
+    if transpose and qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=w.device)
+    _check(lib().fp8_quant_block(_ptr(w), rows, cols, _ld(w), int(scale_mode), _ptr(q), _ld(q),
+                                 _ptr(qt) if transpose else None, _ld(qt) if transpose else 0,
+                                 _ptr(s), _ld(s), _stream()), "fp8_quant_block")
+    return q, s, qt
+
+
+# ---- GEMM -----------------------------------------------------------------------
+
+def gemm_workspace_bytes(M, N, K):
+    return int(lib().fp8_gemm_workspace_bytes(M, N, K))
+
+
+def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_BF16, d=None,
+                         workspace=None):
+    """D[m,n] = sum_g sa[g,m] * SB(n,g) * sum_{k in g} dec(a[m,k]) dec(b[n,k]).
+    a [M, K] and b [N, K] uint8 codes; sa [K/128, >=M] fp32; sb fp32 read as
+    SB(n,g) = sb[(n//128)*sb_s0 + g*sb_s1] (BLOCK) or sb[g*sb_s0 + n] (TILE)."""
+    _dev(a, "a", torch.uint8)
+    _dev(b, "b", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(sb, "sb", torch.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if d is None:
+        d = torch.empty((M, N), dtype=dt, device=a.device)
+    need = gemm_workspace_bytes(M, N, K)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().fp8_gemm_blockscaled(M, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa), _ptr(b), _ld(b),
+                                      _ptr(sb), int(bscale_kind), int(sb_s0), int(sb_s1), _ptr(d),
+                                      _ld(d), int(out_dtype),
+                                      _ptr(workspace) if workspace is not None else None, ws_bytes,
+                                      _stream()), "fp8_gemm_blockscaled")
+    return d
+
+
+def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None, d=None):
+    """Grouped block-scaled GEMM: rows offsets[e]..offsets[e+1]-1 of a use
+    expert e's codes b[e] [N, K] and block scales sb[e] [N/128, K/128].
+    offsets is an int32 device tensor; rows_bound defaults to a.shape[0]."""
+    _dev(offsets, "offsets", torch.int32)
+    _dev(a, "a", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(b, "b", torch.uint8)
+    _dev(sb, "sb", torch.float32)
+    G, N, K = b.shape
+    if not b.is_contiguous() or not sb.is_contiguous():
+        raise ValueError("b and sb must be contiguous [G, N, K] / [G, N/128, K/128]")
+    rows = a.shape[0] if rows_bound is None else int(rows_bound)
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if d is None:
+        d = torch.empty((rows, N), dtype=dt, device=a.device)
+    _check(lib().fp8_grouped_gemm(G, rows, N, K, _ptr(offsets), _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                                  _ptr(b), _ptr(sb), _ptr(d), _ld(d), int(out_dtype), _stream()),
+           "fp8_grouped_gemm")
+    return d
+
+
+# ---- the three GEMMs of a Linear ---------------------------------------------------
+
+def linear_fprop(qx, sx, qw, sw, out_dtype=OUT_BF16):
+    """Y = X W^T from quant_tile(X, ROW) and quant_block(W)."""
+    return fp8_gemm_blockscaled(qx, sx, qw, sw, BSCALE_BLOCK, _ld(sw), 1, out_dtype)
+
+
+def linear_dgrad(qdy, sdy, qwt, sw, out_dtype=OUT_F32):
+    """dX = dY W from quant_tile(dY, ROW) and the transposed codes qt of
+    quant_block(W) (scales of W read transposed)."""
+    return fp8_gemm_blockscaled(qdy, sdy, qwt, sw, BSCALE_BLOCK, 1, _ld(sw), out_dtype)
+
+
+def linear_wgrad(qdyt, sdyt, qxt, sxt, out_dtype=OUT_F32):
+    """dW = dY^T X from quant_tile(dY, COL) and quant_tile(X, COL)."""
+    return fp8_gemm_blockscaled(qdyt, sdyt, qxt, sxt, BSCALE_TILE, _ld(sxt), 0, out_dtype)

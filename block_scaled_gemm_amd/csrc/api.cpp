@@ -1,0 +1,200 @@
+// api.cpp -- the C ABI of libfp8bs.so (declared in include/fp8bs.h).
+//
+// Every entry point validates its arguments on the host first (no HIP call
+// is made for a rejected call), then checks that the current device is a
+// gfx950, then enqueues its kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fp8bs.h"
+#include "kernels.h"
+
+#define FP8BS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// gfx950 check, cached per device ordinal.
+int check_device() {
+    static std::mutex mu;
+    static int cache[64];  // 0 unknown, 1 ok, 2 not ok
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8BS_ERR_DEVICE;
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        if (cache[dev] == 1) return FP8BS_OK;
+        if (cache[dev] == 2) return FP8BS_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BS_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        cache[dev] = ok ? 1 : 2;
+    }
+    return ok ? FP8BS_OK : FP8BS_ERR_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
+
+}  // namespace
+
+FP8BS_EXPORT int fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+FP8BS_EXPORT const char* fp8bs_status_string(int status) {
+    switch (status) {
+        case FP8BS_OK: return "ok";
+        case FP8BS_ERR_ARG: return "invalid argument (null pointer, bad enum, negative size or leading dimension too small)";
+        case FP8BS_ERR_SHAPE: return "a grouped dimension is not a multiple of 128";
+        case FP8BS_ERR_ALIGN: return "pointer or leading dimension misaligned";
+        case FP8BS_ERR_WORKSPACE: return "workspace missing or too small";
+        case FP8BS_ERR_DEVICE: return "current device is not a gfx950 GPU";
+        case FP8BS_ERR_HIP: return "HIP reported an error while launching";
+        default: return "unknown status";
+    }
+}
+
+FP8BS_EXPORT int fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream) {
+    if (n < 0 || (n > 0 && (!x || !q))) return FP8BS_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 4)) return FP8BS_ERR_ALIGN;
+    if (n == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_cast(x, n, q, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                                int scale_mode, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                void* stream) {
+    if (axis != FP8BS_AXIS_ROW && axis != FP8BS_AXIS_COL) return FP8BS_ERR_ARG;
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (rows < 0 || cols < 0) return FP8BS_ERR_ARG;
+    if (rows > 0 && cols > 0 && (!x || !q || !s)) return FP8BS_ERR_ARG;
+    if (ldx < cols) return FP8BS_ERR_ARG;
+    if (axis == FP8BS_AXIS_ROW) {
+        if (cols % 128 != 0) return FP8BS_ERR_SHAPE;
+        if (ldq < cols || lds < rows) return FP8BS_ERR_ARG;
+    } else {
+        if (rows % 128 != 0) return FP8BS_ERR_SHAPE;
+        if (ldq < rows || lds < cols) return FP8BS_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || ldx % 8 != 0 || ldq % 16 != 0)
+        return FP8BS_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_quant_tile(x, rows, cols, ldx, axis, scale_mode == FP8BS_SCALE_POW2, q,
+                                               ldq, s, lds, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw, int scale_mode,
+                                 uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s, int64_t lds,
+                                 void* stream) {
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (rows < 0 || cols < 0) return FP8BS_ERR_ARG;
+    if (rows > 0 && cols > 0 && (!w || !q || !s)) return FP8BS_ERR_ARG;
+    if (cols % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (ldw < cols || ldq < cols || lds < cols / 128 || (qt && ldqt < rows)) return FP8BS_ERR_ARG;
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 4) || ldw % 8 != 0 ||
+        ldq % 16 != 0 || (qt && ldqt % 16 != 0))
+        return FP8BS_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_quant_block(w, rows, cols, ldw, scale_mode == FP8BS_SCALE_POW2, q, ldq, qt,
+                                                ldqt, s, lds, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
+    return fp8bs::gemm_workspace(M, N, K);
+}
+
+namespace {
+
+int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                      int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb, void* d, int64_t ldd,
+                      int out_dtype) {
+    if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_ARG;
+    if (M > 0 && N > 0) {
+        if (!d) return FP8BS_ERR_ARG;
+        if (K > 0 && (!a || !sa || !b || !sb)) return FP8BS_ERR_ARG;
+    }
+    if (K % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (lda < K || ldb < K || ldd < N || ldsa < M) return FP8BS_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
+        (K > 0 && (lda % 16 != 0 || ldb % 16 != 0)) || ldd % 4 != 0)
+        return FP8BS_ERR_ALIGN;
+    return FP8BS_OK;
+}
+
+}  // namespace
+
+FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                      const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                      const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1, void* d,
+                                      int64_t ldd, int out_dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
+    if (int r = check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
+    if (M == 0 || N == 0) return FP8BS_OK;
+    const size_t need = fp8_gemm_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP8BS_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+    if (int r = check_device()) return r;
+    fp8bs::GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+    g.b = b;
+    g.ldb = ldb;
+    g.sb = sb;
+    g.bscale_kind = bscale_kind;
+    g.sb_s0 = sb_s0;
+    g.sb_s1 = sb_s1;
+    g.d = d;
+    g.ldd = ldd;
+    g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.splits = need > 0 ? fp8bs::gemm_splits(M, N, K) : 1;
+    g.ws = (float*)workspace;
+    g.ws_ld = (N + 3) / 4 * 4;
+    return hip_status(fp8bs::launch_gemm(g, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K, const int32_t* offsets,
+                                  const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                                  const float* sb, void* d, int64_t ldd, int out_dtype, void* stream) {
+    if (G < 0 || rows_bound < 0) return FP8BS_ERR_ARG;
+    if (G > 0 && !offsets) return FP8BS_ERR_ARG;
+    if (N % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (int r = check_gemm_common(rows_bound, N, K, a, lda, sa, ldsa, b, K, sb, d, ldd, out_dtype)) return r;
+    if (!aligned(offsets, 4)) return FP8BS_ERR_ALIGN;
+    if (G == 0 || N == 0 || rows_bound == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    fp8bs::GemmArgs g{};
+    g.M = rows_bound;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+    g.b = b;
+    g.ldb = K;
+    g.sb = sb;
+    g.bscale_kind = FP8BS_BSCALE_BLOCK;
+    g.d = d;
+    g.ldd = ldd;
+    g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.splits = 1;
+    g.offsets = offsets;
+    g.G = G;
+    g.b_estride = N * K;
+    g.sb_estride = (N / 128) * (K / 128);
+    return hip_status(fp8bs::launch_grouped_gemm(g, (hipStream_t)stream));
+}

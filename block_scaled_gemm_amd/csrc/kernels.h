@@ -1,0 +1,56 @@
+// kernels.h -- internal launch interface between the C ABI (api.cpp) and the
+// HIP kernels.  Launchers assume their arguments were validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_cast(const float* x, int64_t n, uint8_t* q, hipStream_t st);
+
+hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                             bool pow2, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             hipStream_t st);
+
+hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw, bool pow2,
+                              uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
+                              int64_t lds, hipStream_t st);
+
+// Everything a block-scaled GEMM launch needs.  For a grouped launch,
+// `offsets` is non-null, `G` experts share N and K, expert e's codes start at
+// b + e*b_estride and its block scales at sb + e*sb_estride.
+struct GemmArgs {
+    int64_t M, N, K;
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ldsa;
+    const uint8_t* b;
+    int64_t ldb;
+    const float* sb;
+    int bscale_kind;  // 0 block, 1 tile
+    int64_t sb_s0, sb_s1;
+    void* d;
+    int64_t ldd;
+    int out_f32;  // 0 bf16, 1 fp32
+    // split-K (dense only): partials in `ws`, row stride ws_ld floats
+    float* ws;
+    int splits;
+    int64_t ws_ld;
+    // grouped
+    const int32_t* offsets;
+    int G;
+    int64_t b_estride, sb_estride;
+};
+
+// Split count the dense GEMM uses for this shape (1 = no split).
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+// Workspace bytes the dense GEMM needs for this shape.
+size_t gemm_workspace(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);
+
+}  // namespace fp8bs

@@ -1,0 +1,246 @@
+// quant.hip -- online fine-grained quantisation kernels for gfx950.
+//
+// The quantisers are HBM-bound: each element is read once as bf16 (2 B) and
+// written once as an E4M3 code (1 B), plus 4 B of scale per group.  Every
+// kernel keeps its loads 16 B per lane and fully coalesced, finds the group
+// max with packed 16-bit maxima and DPP reductions inside a 16-lane row,
+// and rounds with e4m3_code (see device.h).
+#include "device.h"
+#include "kernels.h"
+
+namespace fp8bs {
+
+// ---- plain cast ------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, int64_t n,
+                                                   uint8_t* __restrict__ q) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        const float4 v = *(const float4*)(x + i);
+        *(uint32_t*)(q + i) = pack4(v.x, v.y, v.z, v.w);
+    } else {
+        for (int64_t j = i; j < n; j++) q[j] = (uint8_t)e4m3_code(x[j]);
+    }
+}
+
+hipError_t launch_cast(const float* x, int64_t n, uint8_t* q, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = (n + 1023) / 1024;
+    hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, q);
+    return hipGetLastError();
+}
+
+// ---- 1x128 groups along rows ---------------------------------------------------------
+//
+// A workgroup covers 16 rows x 512 columns: each wave takes 4 rows, each
+// 16-lane DPP row one 128-element group (8 bf16 = 16 B per lane).  The four
+// row loads are issued before any reduction so 64 B per lane are in flight.
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ldx,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t lds,
+                                                        int64_t col_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tile_c = blockIdx.x % col_tiles;
+    const int64_t tile_r = blockIdx.x / col_tiles;
+    const int64_t col = tile_c * 512 + lane * 8;
+    const bool colok = col < cols;
+    const int64_t r0 = tile_r * 16 + wave * 4;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int64_t r = r0 + i;
+        v[i] = (colok && r < rows) ? *(const uint4*)(x + r * ldx + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t am = row16_max(absmax8(v[i]));
+        const GroupScale gs = group_scale(am, POW2);
+        const int64_t r = r0 + i;
+        if (colok && r < rows) {
+            *(uint2*)(q + r * ldq + col) = quant8(v[i], gs.inv);
+            if ((lane & 15) == 0) s[(col >> 7) * lds + r] = gs.s;
+        }
+    }
+}
+
+// ---- 128x1 groups down columns, codes written transposed -------------------------------
+//
+// A workgroup covers one 128-row group x 64 columns.  Load: wave w, lane
+// L reads rows 32w + 16it + 2p + {0,1} (p = L%8, it = 0..1) of the 8-column
+// chunk L/8, packs the two rows' values of each column into one dword and
+// stores it to LDS at column-major position (column c, row pair rp) with the
+// 16-byte chunk index of rp XOR-swizzled by 2*(c/8): the 32 lanes of each
+// half-wave then hit 32 different banks.  Process: each 16-lane DPP row
+// reads one column (lane l: rows 8l..8l+7, one 16 B LDS read), reduces the
+// column's amax, and writes 8 codes, so the 16 lanes store the group's 128
+// codes as one contiguous 128 B run of the transposed output.
+
+__device__ __forceinline__ uint32_t col_lds_index(int c, int rp) {
+    const int chunk = (rp >> 2) ^ ((c >> 3) << 1);
+    return (uint32_t)(c * 64 + chunk * 4 + (rp & 3));
+}
+
+__device__ __forceinline__ uint4 load_chunk_masked(const uint16_t* __restrict__ p, int64_t col,
+                                                   int64_t cols) {
+    if (col + 8 <= cols) return *(const uint4*)p;
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 8; i++)
+        if (col + i < cols) w[i >> 1] |= (uint32_t)p[i] << (16 * (i & 1));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ldx,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t lds,
+                                                        int64_t col_tiles) {
+    __shared__ uint32_t tile[64 * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t g = blockIdx.x / col_tiles;
+    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
+
+    {
+        const int chunk = lane >> 3, p = lane & 7;
+        const int64_t col = c0 + chunk * 8;
+        const bool ok = col < cols;
+        uint4 lo[2], hi[2];
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const int64_t r = g * 128 + wave * 32 + it * 16 + 2 * p;
+            const uint16_t* src = x + r * ldx + col;
+            lo[it] = ok ? load_chunk_masked(src, col, cols) : make_uint4(0, 0, 0, 0);
+            hi[it] = ok ? load_chunk_masked(src + ldx, col, cols) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const int rp = wave * 16 + it * 8 + p;
+            const uint32_t a[4] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w};
+            const uint32_t b[4] = {hi[it].x, hi[it].y, hi[it].z, hi[it].w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int c = chunk * 8 + 2 * j;
+                tile[col_lds_index(c, rp)] = perm(b[j], a[j], 0x05040100u);      // col c
+                tile[col_lds_index(c + 1, rp)] = perm(b[j], a[j], 0x07060302u);  // col c+1
+            }
+        }
+    }
+    __syncthreads();
+
+    const int l = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+        const int c = wave * 16 + it * 4 + (lane >> 4);
+        const uint4 v = *(const uint4*)&tile[col_lds_index(c, 4 * l)];
+        const uint32_t am = row16_max(absmax8(v));
+        const GroupScale gs = group_scale(am, POW2);
+        const int64_t col = c0 + c;
+        if (col < cols) {
+            *(uint2*)(q + col * ldq + g * 128 + 8 * l) = quant8(v, gs.inv);
+            if (l == 0) s[g * lds + col] = gs.s;
+        }
+    }
+}
+
+// ---- 128x128 blocks ----------------------------------------------------------------------
+//
+// A workgroup quantises one block.  Thread t owns the 8x8 sub-block at rows
+// 8(t/16).., columns 8(t%16)..; each load instruction reads 4 full 256 B
+// row segments.  The block amax is a thread max, a wave max, then a max over
+// the 4 waves through LDS.  The optional transposed copy is an in-register
+// 8x8 byte transpose, each thread storing 8 columns x 8 rows.
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ w, int64_t rows,
+                                                          int64_t ldw, uint8_t* __restrict__ q,
+                                                          int64_t ldq, uint8_t* __restrict__ qt,
+                                                          int64_t ldqt, float* __restrict__ s,
+                                                          int64_t lds, int64_t col_blocks) {
+    __shared__ uint32_t wmax[4];
+    const int t = threadIdx.x;
+    const int64_t bi = blockIdx.x / col_blocks, bj = blockIdx.x % col_blocks;
+    const int64_t r0 = bi * 128 + 8 * (t >> 4);
+    const int64_t c0 = bj * 128 + 8 * (t & 15);
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        v[i] = (r0 + i < rows) ? *(const uint4*)(w + (r0 + i) * ldw + c0) : make_uint4(0, 0, 0, 0);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) am = max(am, absmax8(v[i]));
+    am = wave_max(am);
+    if ((t & 63) == 0) wmax[t >> 6] = am;
+    __syncthreads();
+    am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const GroupScale gs = group_scale(am, POW2);
+    if (t == 0) s[bi * lds + bj] = gs.s;
+
+    uint2 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        c[i] = quant8(v[i], gs.inv);
+        if (r0 + i < rows) *(uint2*)(q + (r0 + i) * ldq + c0) = c[i];
+    }
+    if (qt != nullptr) {
+        uint32_t lo[8], hi[8];
+        transpose4x4(c[0].x, c[1].x, c[2].x, c[3].x, lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4(c[4].x, c[5].x, c[6].x, c[7].x, hi[0], hi[1], hi[2], hi[3]);
+        transpose4x4(c[0].y, c[1].y, c[2].y, c[3].y, lo[4], lo[5], lo[6], lo[7]);
+        transpose4x4(c[4].y, c[5].y, c[6].y, c[7].y, hi[4], hi[5], hi[6], hi[7]);
+        const bool full = r0 + 8 <= rows;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            uint8_t* dst = qt + (c0 + j) * ldqt + r0;
+            if (full) {
+                *(uint2*)dst = make_uint2(lo[j], hi[j]);
+            } else {
+                for (int i = 0; i < 8; i++)
+                    if (r0 + i < rows) dst[i] = (uint8_t)((i < 4 ? lo[j] >> (8 * i) : hi[j] >> (8 * (i - 4))) & 0xFF);
+            }
+        }
+    }
+}
+
+// ---- launchers -------------------------------------------------------------------------------
+
+hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                             bool pow2, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (axis == 0) {
+        const int64_t ct = (cols + 511) / 512, rt = (rows + 15) / 16;
+        const dim3 grid((unsigned)(ct * rt));
+        if (pow2)
+            hipLaunchKernelGGL(quant_row_kernel<true>, grid, dim3(256), 0, st, x, rows, cols, ldx, q, ldq, s, lds, ct);
+        else
+            hipLaunchKernelGGL(quant_row_kernel<false>, grid, dim3(256), 0, st, x, rows, cols, ldx, q, ldq, s, lds, ct);
+    } else {
+        const int64_t ct = (cols + 63) / 64, gt = rows / 128;
+        const dim3 grid((unsigned)(ct * gt));
+        if (pow2)
+            hipLaunchKernelGGL(quant_col_kernel<true>, grid, dim3(256), 0, st, x, rows, cols, ldx, q, ldq, s, lds, ct);
+        else
+            hipLaunchKernelGGL(quant_col_kernel<false>, grid, dim3(256), 0, st, x, rows, cols, ldx, q, ldq, s, lds, ct);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw, bool pow2,
+                              uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
+                              int64_t lds, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t cb = cols / 128, rb = (rows + 127) / 128;
+    const dim3 grid((unsigned)(cb * rb));
+    if (pow2)
+        hipLaunchKernelGGL(quant_block_kernel<true>, grid, dim3(256), 0, st, w, rows, ldw, q, ldq, qt, ldqt, s, lds, cb);
+    else
+        hipLaunchKernelGGL(quant_block_kernel<false>, grid, dim3(256), 0, st, w, rows, ldw, q, ldq, qt, ldqt, s, lds, cb);
+    return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,234 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs.so: fine-grained FP8 quantisation and the
+ * block-scaled FP8 GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by host and post id, then the passage):
+ *  - Activations and weights are quantised online: each small group's
+ *    maximum absolute value gives its scaling factor, and the group is then
+ *    cast to FP8 ([qna-131281], passage on deriving the scaling factor and
+ *    quantising online; [why-be-59061], passage on adapting the scale to
+ *    smaller groups to absorb outliers).  The maximum absolute value is
+ *    mapped onto the largest FP8 value ([cameseeing-1171527], passage on
+ *    aligning the input distribution with the FP8 range).
+ *  - Some activations use scales that are integral powers of two
+ *    ([why-be-59061], passage on the input of the Linear after attention and
+ *    the gradient before the MoE down-projection).
+ *  - The backward pass needs activations re-tiled as 128x1 groups along the
+ *    token dimension ([hacks-368261], passage on reading, dequantising,
+ *    transposing and re-quantising activations into 128x1 tiles).
+ *  - All three GEMMs of a Linear -- Fprop, Dgrad, Wgrad -- run in FP8
+ *    ([why-be-59061], Figure 6 passage), taking FP8 inputs and producing
+ *    BF16 or FP32 ([qna-131281], passage on the FP8 Wgrad GEMM).
+ *  - Partial sums are promoted to FP32 every 128 elements of K, where the
+ *    per-group dequantisation is applied ([why-be-59061], passage on the
+ *    128-element interval and the copy of partial results to FP32
+ *    registers; [cameseeing-1171527], Figure 7(b) passage).
+ *  - In decoding, experts see few tokens each and the GEMM is bound by
+ *    memory ([why-be-59061], passage on the decoding stage).
+ *
+ * Page keys: [qna-131281] xn--9g3bo1gtkw0l8ubf92bgle.kr qna post 131281;
+ * [hacks-368261] "9 Amazing Deepseek Hacks", xn--jj0bz6z98ct0a29q.com post
+ * 368261; [cameseeing-1171527] blog.cameseeing.com freeboard post 1171527;
+ * [why-be-59061] and [why-be-50529] why-be.why-be.co.kr as_center posts.
+ *
+ * Conventions for every call:
+ *  - bf16 tensors are passed as their 16-bit patterns (uint16_t); FP8 codes
+ *    are OCP E4M3 ("FN": bias 7, max 448, 0x7F/0xFF NaN, never produced);
+ *    scales are fp32 dequantisation factors: value ~= decode(code) * scale.
+ *  - Every pointer argument except `stream` is DEVICE memory allocated and
+ *    owned by the caller.  The library never allocates, frees or
+ *    synchronises; each call validates its arguments on the host, enqueues
+ *    its kernels on `stream` (a hipStream_t, NULL = the null stream) and
+ *    returns.  Device faults surface at the caller's next synchronisation.
+ *  - Inputs are read only; outputs are completely overwritten; inputs and
+ *    outputs must not overlap.
+ *  - On any error the call returns a nonzero status and enqueues nothing.
+ *  - Calls are reentrant; calls on different streams may run concurrently.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_ARG = 1,       /* null pointer, bad enum, negative size, ld too small */
+    FP8BS_ERR_SHAPE = 2,     /* a grouped dimension is not a multiple of 128 */
+    FP8BS_ERR_ALIGN = 3,     /* pointer or leading dimension misaligned */
+    FP8BS_ERR_WORKSPACE = 4, /* workspace missing or too small */
+    FP8BS_ERR_DEVICE = 5,    /* current device is not gfx950 / no device */
+    FP8BS_ERR_HIP = 6        /* a HIP launch reported an error */
+};
+
+/* Group orientation of fp8_quant_tile. */
+enum {
+    FP8BS_AXIS_ROW = 0, /* 1x128 groups along the contiguous dimension */
+    FP8BS_AXIS_COL = 1  /* 128x1 groups down the columns; codes transposed */
+};
+
+/* Scale mode. */
+enum {
+    FP8BS_SCALE_FP32 = 0, /* s = amax/448 (fp32 division), codes of x*(448/amax) */
+    FP8BS_SCALE_POW2 = 1  /* s = smallest power of two with amax <= 448*s */
+};
+
+/* GEMM output type. */
+enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_F32 = 1 };
+
+/* How the B operand's scales are addressed (SB(n, g) for column n of the
+ * output and K group g). */
+enum {
+    FP8BS_BSCALE_BLOCK = 0, /* 128x128 blocks: SB(n,g) = sb[(n/128)*sb_s0 + g*sb_s1] */
+    FP8BS_BSCALE_TILE = 1   /* 128x1 tiles:    SB(n,g) = sb[g*sb_s0 + n]            */
+};
+
+/* Version of this ABI (FP8BS_ABI_VERSION). */
+int fp8bs_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *fp8bs_status_string(int status);
+
+/*
+ * fp8_cast_e4m3 -- q[i] = E4M3 code of x[i] for i < n: nearest value, ties
+ * to the even code, |x| >= 448 saturating to +-448, sign kept for values
+ * that round to zero.  This is the final rounding step of every quantiser
+ * (the cast to FP8 of [qna-131281]'s online quantisation), exposed on its
+ * own.  x: fp32 [n], finite, 16-byte aligned; q: uint8 [n], 4-byte aligned.
+ * Errors: ERR_ARG (null pointer with n > 0, n < 0), ERR_DEVICE, ERR_HIP.
+ */
+int fp8_cast_e4m3(const float *x, int64_t n, uint8_t *q, void *stream);
+
+/*
+ * fp8_quant_tile -- online quantisation of activations in 1x128 or 128x1
+ * groups ([qna-131281] fine-grained quantisation passage; [hacks-368261]
+ * 128x1 tiles for the backward pass).
+ *
+ *   x      bf16 bits [rows][ldx], row-major.
+ *   axis   FP8BS_AXIS_ROW: group (r, g) = x[r][128g .. 128g+127];
+ *            q is [rows][ldq] (same orientation as x);
+ *            s[g*lds + r] is the scale of group (r, g), g < cols/128.
+ *            cols must be a multiple of 128; rows is any value >= 0.
+ *          FP8BS_AXIS_COL: group (g, c) = x[128g .. 128g+127][c];
+ *            q is written TRANSPOSED, [cols][ldq], so q[c][128g + i] is the
+ *            code of x[128g + i][c] and each group is 128 contiguous bytes;
+ *            s[g*lds + c] is the scale of group (g, c), g < rows/128.
+ *            rows must be a multiple of 128; cols is any value >= 0.
+ *   scale_mode  FP8BS_SCALE_FP32 or FP8BS_SCALE_POW2.
+ *   Group amax is floored at 448*2^-126 so an all-zero group gets
+ *   s = 2^-126 and zero codes.
+ *
+ * Alignment: x and q 16-byte aligned; ldx a multiple of 8 elements; ldq a
+ * multiple of 16 bytes; s 4-byte aligned.  ldx >= cols; ldq >= cols (ROW)
+ * or >= rows (COL); lds >= rows (ROW) or >= cols (COL).
+ * Errors: ERR_ARG, ERR_SHAPE (grouped dimension % 128 != 0), ERR_ALIGN,
+ * ERR_DEVICE, ERR_HIP.
+ */
+int fp8_quant_tile(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                   int axis, int scale_mode, uint8_t *q, int64_t ldq, float *s,
+                   int64_t lds, void *stream);
+
+/*
+ * fp8_quant_block -- online quantisation of a weight matrix in 128x128
+ * blocks (the weight grouping of the fine-grained quantisation,
+ * [qna-131281] and [why-be-59061] passages on fine-grained scaling).
+ *
+ *   w     bf16 bits [rows][ldw]; cols must be a multiple of 128; a last
+ *         partial block-row (rows % 128 != 0) holds only the rows present.
+ *   q     codes [rows][ldq].
+ *   qt    optional (NULL = skip) transposed copy of the codes, [cols][ldqt]:
+ *         qt[c][r] == q[r][c].  A 128x128 block's scale does not depend on
+ *         orientation, so qt with the transposed scales is the quantised W^T
+ *         that Dgrad multiplies by.
+ *   s     s[(r/128)*lds + c/128] is the scale of the block holding (r, c).
+ *
+ * Alignment: w, q, qt 16-byte aligned; ldw a multiple of 8; ldq and ldqt
+ * multiples of 16; ldw, ldq >= cols; ldqt >= rows; lds >= cols/128.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_quant_block(const uint16_t *w, int64_t rows, int64_t cols,
+                    int64_t ldw, int scale_mode, uint8_t *q, int64_t ldq,
+                    uint8_t *qt, int64_t ldqt, float *s, int64_t lds,
+                    void *stream);
+
+/*
+ * fp8_gemm_blockscaled -- block-scaled FP8 GEMM with FP32 promotion every
+ * 128-element K group ([why-be-59061] 128-element interval passage;
+ * [cameseeing-1171527] Figure 7(b) passage; [why-be-59061] Figure 6
+ * passage for Fprop / Dgrad / Wgrad):
+ *
+ *   D[m][n] = sum_{g < K/128} sa[g*ldsa + m] * SB(n, g) *
+ *             sum_{k = 128g}^{128g+127} dec(a[m*lda + k]) * dec(b[n*ldb + k])
+ *
+ * Each group's inner sum is formed on the matrix cores and multiplied by its
+ * two scales into an FP32 accumulator, which is rounded once to the output
+ * type (bf16: round to nearest even).
+ *   a      E4M3 codes [M][lda], K contiguous.
+ *   sa     per-row scale of each K group of a: sa[g*ldsa + m].
+ *   b      E4M3 codes [N][ldb], K contiguous ("TN": both operands K-major).
+ *   sb, bscale_kind, sb_s0, sb_s1   scales of b, addressed as SB(n, g)
+ *          above.  Fprop (B = W from fp8_quant_block):  BLOCK, s0 = lds, s1 = 1.
+ *          Dgrad (B = qt of W, its scales transposed): BLOCK, s0 = 1, s1 = lds.
+ *          Wgrad (B from fp8_quant_tile COL):          TILE,  s0 = lds.
+ *   d      output [M][ldd], bf16 bits (FP8BS_OUT_BF16) or fp32 (FP8BS_OUT_F32).
+ *   workspace  device scratch of at least fp8_gemm_workspace_bytes(M, N, K)
+ *          bytes (may be NULL when that is 0); it holds split-K partials
+ *          when K is long and the output small.  The reduction over splits
+ *          is in a fixed order, so results are run-to-run deterministic.
+ * K must be a multiple of 128 (K == 0 writes zeros); M, N >= 0 (0 = no-op).
+ * Alignment: a, b 16-byte aligned, lda and ldb multiples of 16 (when
+ * K > 0); d 16-byte
+ * aligned, ldd a multiple of 4 elements; sa, sb 4-byte aligned.
+ * lda, ldb >= K; ldd >= N; ldsa >= M.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t *a,
+                         int64_t lda, const float *sa, int64_t ldsa,
+                         const uint8_t *b, int64_t ldb, const float *sb,
+                         int bscale_kind, int64_t sb_s0, int64_t sb_s1,
+                         void *d, int64_t ldd, int out_dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fp8_gemm_blockscaled needs for this shape (0 = none). */
+size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * fp8_grouped_gemm -- the block-scaled GEMM for a group of MoE experts
+ * (expert GEMMs in FP8, [why-be-59061] passage on the activation gradient
+ * before the MoE down-projection; few, memory-bound tokens per expert in
+ * decoding, [why-be-59061] decoding passage).  Rows offsets[e] ..
+ * offsets[e+1]-1 of a (and of d) belong to expert e:
+ *
+ *   D[m][n] = sum_g sa[g*ldsa + m] * sb[e][n/128][g] *
+ *             sum_{k in g} dec(a[m*lda + k]) * dec(b[e][n][k])
+ *
+ *   offsets  DEVICE int32 [G+1], offsets[0] = 0, non-decreasing,
+ *            offsets[G] <= rows_bound.  Read only on the device, so no host
+ *            synchronisation is needed; offsets that break this contract
+ *            give undefined results.  Empty experts are allowed.
+ *   rows_bound  host-side upper bound of offsets[G] (rows of a, sa, d).
+ *   a, sa    codes [rows][lda] and scales sa[g*ldsa + m] of all rows
+ *            (fp8_quant_tile ROW of the rows gathered per expert).
+ *   b        codes [G][N][K] (contiguous), sb  block scales [G][N/128][K/128].
+ *   d        output [rows][ldd], bf16 or fp32 as out_dtype.
+ * N and K must be multiples of 128.  Alignment as fp8_gemm_blockscaled;
+ * ldsa >= rows_bound.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K,
+                     const int32_t *offsets, const uint8_t *a, int64_t lda,
+                     const float *sa, int64_t ldsa, const uint8_t *b,
+                     const float *sb, void *d, int64_t ldd, int out_dtype,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8BS_H */

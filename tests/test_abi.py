@@ -1,0 +1,150 @@
+"""The C ABI of libfp8bs.so: it loads, exports every function include/fp8bs.h
+declares, and rejects bad arguments on the host before any HIP call (so
+these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_gemm_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, ARG, SHAPE, ALIGN, WORKSPACE, DEVICE, HIP = range(7)
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8\w*)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
+              "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
+              "fp8bs_abi_version", "fp8bs_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bs.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in fp8bs.h but not exported"
+
+
+def test_only_the_abi_is_exported():
+    out = os.popen(f"nm -D --defined-only {bs.LIB_PATH}").read().split("\n")
+    names = {l.split()[-1] for l in out if " T " in l}
+    assert names, "nm printed nothing"
+    assert names <= set(declared_functions()), names - set(declared_functions())
+
+
+def test_version_and_status_strings():
+    assert bs.abi_version() == 1
+    for s in range(7):
+        assert bs.status_string(s)
+    assert "unknown" in bs.status_string(99)
+
+
+def _tile(**kw):
+    a = dict(x=FAKE, rows=256, cols=256, ldx=256, axis=0, mode=0, q=FAKE, ldq=256, s=FAKE, lds=256)
+    a.update(kw)
+    return bs.lib().fp8_quant_tile(a["x"], a["rows"], a["cols"], a["ldx"], a["axis"], a["mode"],
+                                   a["q"], a["ldq"], a["s"], a["lds"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(axis=2), ARG), (dict(mode=3), ARG), (dict(x=None), ARG), (dict(q=None), ARG),
+    (dict(s=None), ARG), (dict(rows=-1), ARG), (dict(ldx=128), ARG), (dict(ldq=128), ARG),
+    (dict(lds=100), ARG), (dict(cols=200, ldx=256), SHAPE), (dict(axis=1, rows=200), SHAPE),
+    (dict(x=FAKE + 2), ALIGN), (dict(q=FAKE + 8), ALIGN), (dict(s=FAKE + 2), ALIGN),
+    (dict(ldx=260), ALIGN), (dict(ldq=264), ALIGN),
+    (dict(rows=0), OK), (dict(cols=0, ldx=0, ldq=0), OK),
+])
+def test_quant_tile_validation(kw, want):
+    assert _tile(**kw) == want
+
+
+def _block(**kw):
+    a = dict(w=FAKE, rows=256, cols=256, ldw=256, mode=0, q=FAKE, ldq=256, qt=None, ldqt=0, s=FAKE, lds=2)
+    a.update(kw)
+    return bs.lib().fp8_quant_block(a["w"], a["rows"], a["cols"], a["ldw"], a["mode"], a["q"], a["ldq"],
+                                    a["qt"], a["ldqt"], a["s"], a["lds"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mode=2), ARG), (dict(w=None), ARG), (dict(lds=1), ARG), (dict(qt=FAKE, ldqt=128), ARG),
+    (dict(cols=192, ldw=256), SHAPE), (dict(qt=FAKE + 4, ldqt=256), ALIGN),
+    (dict(qt=FAKE, ldqt=264), ALIGN), (dict(ldw=260), ALIGN), (dict(rows=0), OK),
+])
+def test_quant_block_validation(kw, want):
+    assert _block(**kw) == want
+
+
+def _gemm(**kw):
+    a = dict(M=256, N=256, K=512, a=FAKE, lda=512, sa=FAKE, ldsa=256, b=FAKE, ldb=512, sb=FAKE,
+             kind=0, s0=4, s1=1, d=FAKE, ldd=256, out=0, ws=None, wsb=0)
+    a.update(kw)
+    return bs.lib().fp8_gemm_blockscaled(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["ldsa"],
+                                         a["b"], a["ldb"], a["sb"], a["kind"], a["s0"], a["s1"], a["d"],
+                                         a["ldd"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
+    (dict(M=-1), ARG), (dict(lda=256), ARG), (dict(ldd=128), ARG), (dict(ldsa=100), ARG),
+    (dict(K=500, lda=512, ldb=512), SHAPE), (dict(a=FAKE + 8), ALIGN), (dict(d=FAKE + 4), ALIGN),
+    (dict(lda=520), ALIGN), (dict(ldd=258), ALIGN), (dict(sa=FAKE + 1), ALIGN),
+    (dict(M=0), OK), (dict(N=0), OK),
+    (dict(M=256, N=256, K=65536, lda=65536, ldb=65536), WORKSPACE),
+])
+def test_gemm_validation(kw, want):
+    assert _gemm(**kw) == want
+
+
+def test_workspace_query():
+    assert bs.gemm_workspace_bytes(4096, 18432, 7168) == 0
+    need = bs.gemm_workspace_bytes(256, 256, 65536)
+    assert need >= 2 * 256 * 256 * 4
+    assert bs.gemm_workspace_bytes(256, 256, 100) == 0
+
+
+def _grouped(**kw):
+    a = dict(G=4, rows=512, N=256, K=512, off=FAKE, a=FAKE, lda=512, sa=FAKE, ldsa=512, b=FAKE,
+             sb=FAKE, d=FAKE, ldd=256, out=0)
+    a.update(kw)
+    return bs.lib().fp8_grouped_gemm(a["G"], a["rows"], a["N"], a["K"], a["off"], a["a"], a["lda"],
+                                     a["sa"], a["ldsa"], a["b"], a["sb"], a["d"], a["ldd"], a["out"],
+                                     None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=-1), ARG), (dict(off=None), ARG), (dict(N=200, ldd=256), SHAPE),
+    (dict(K=500, lda=512), SHAPE), (dict(ldsa=100), ARG), (dict(off=FAKE + 2), ALIGN),
+    (dict(G=0), OK), (dict(rows=0), OK),
+])
+def test_grouped_validation(kw, want):
+    assert _grouped(**kw) == want
+
+
+def test_cast_validation():
+    L = bs.lib()
+    assert L.fp8_cast_e4m3(None, 10, FAKE, None) == ARG
+    assert L.fp8_cast_e4m3(FAKE, -1, FAKE, None) == ARG
+    assert L.fp8_cast_e4m3(FAKE + 4, 10, FAKE, None) == ALIGN
+    assert L.fp8_cast_e4m3(FAKE, 10, FAKE + 2, None) == ALIGN
+    assert L.fp8_cast_e4m3(None, 0, None, None) == OK
+
+
+def test_no_device_is_reported():
+    """Valid arguments on a machine without a GPU stop at the device check
+    (the fake pointers are never handed to a kernel)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this check is for GPU-less hosts")
+    assert _tile() == DEVICE
+    assert _gemm() == DEVICE

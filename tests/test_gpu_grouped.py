@@ -1,0 +1,91 @@
+"""GPU grouped (MoE expert) GEMM against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_gemm_amd import inputs
+from gpu_util import workload, bf16_f64, dev, dev_bf16, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def out_f64(t):
+    h = host(t)
+    return bf16_f64(h) if h.dtype == np.uint16 else h.astype(np.float64)
+
+
+def quant_experts(hip, orc, Xcat, W, mode):
+    G, N, K = W.shape
+    qx, sx = hip.fp8_quant_tile(dev_bf16(Xcat), hip.AXIS_ROW, mode)
+    wqx, wsx = orc.quant_tile(Xcat, 0, mode)
+    np.testing.assert_array_equal(host(qx), wqx)
+    np.testing.assert_array_equal(host(sx), wsx)
+    qw, sw, _ = hip.fp8_quant_block(dev_bf16(W.reshape(G * N, K)), mode)
+    wqw, wsw, _ = orc.quant_block(W.reshape(G * N, K), mode)
+    np.testing.assert_array_equal(host(qw), wqw)
+    np.testing.assert_array_equal(host(sw), wsw)
+    return (qx, sx, qw.view(G, N, K), sw.view(G, N // 128, K // 128),
+            wqx, wsx, wqw.reshape(G, N, K), wsw.reshape(G, N // 128, K // 128))
+
+
+@pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
+def test_grouped_small_with_empty_experts(hip, orc, out):
+    """6 experts with 0, 1, 130, 0, 257 and 40 rows (empty experts, a single
+    row, ragged tiles), N = 256, K = 512, power-of-two scales."""
+    counts = [0, 1, 130, 0, 257, 40]
+    offsets = np.zeros(len(counts) + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    Xcat = inputs.random_bf16(201, (int(offsets[-1]), 512))
+    W = inputs.random_bf16(202, (len(counts), 256, 512), sd=0.02, outliers=False)
+    qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, out)
+    r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
+    tol = 1e-3 if out == 1 else 8e-3
+    for e in range(len(counts)):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            err = oracle.max_rel_err(out_f64(y)[r0:r1], r[r0:r1])
+            assert err <= tol, (e, err)
+
+
+def test_grouped_rows_beyond_offsets_untouched(hip, orc):
+    """Rows past offsets[G] (rows_bound larger than the routed rows) are not
+    written."""
+    offsets = np.array([0, 100, 160], np.int32)
+    Xcat = inputs.random_bf16(203, (200, 256))
+    W = inputs.random_bf16(204, (2, 128, 256), sd=0.02, outliers=False)
+    qx, sx, qw, sw, *_ = quant_experts(hip, orc, Xcat, W, 0)
+    d = torch.full((200, 128), 3.0, dtype=torch.float32, device="cuda")
+    hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 1, rows_bound=200, d=d)
+    assert torch.all(d[160:] == 3.0).item()
+
+
+def _check_sampled(hip, orc, data, mode, tag):
+    Xcat, W, offsets = data["Xcat"], data["W"], data["offsets"]
+    qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, mode)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 0)
+    rows, N = y.shape
+    rng = np.random.default_rng(7)
+    mi = rng.integers(0, rows, 3000)
+    ni = rng.integers(0, N, 3000)
+    # first and last row of every expert
+    starts = offsets[:-1][np.diff(offsets) > 0]
+    ends = offsets[1:][np.diff(offsets) > 0] - 1
+    mi = np.concatenate([mi, starts, ends])
+    ni = np.concatenate([ni, rng.integers(0, N, starts.size + ends.size)])
+    r = orc.grouped_gemm_entries(offsets, wqx, wsx, wqw, wsw, mi, ni)
+    err = oracle.max_rel_err(out_f64(y)[mi, ni], r)
+    log(f"{tag}: sampled max rel err {err:.3e}")
+    assert err <= 8e-3
+
+
+def test_grouped_upproj_full_size(hip, orc):
+    """Workload 3: 32 local experts of a top-8-of-256 routing of 4096
+    tokens, N = 4096, K = 7168, power-of-two scales, bf16 out."""
+    _check_sampled(hip, orc, workload("grouped_upproj"), 1, "grouped up-proj")
+
+
+def test_decode_grouped_full_size(hip, orc):
+    """Workload 4a: 64 experts with 1..256 rows each, N = 2048, K = 7168."""
+    _check_sampled(hip, orc, workload("decode_grouped"), 0, "decode grouped")
