@@ -28,6 +28,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 SCALE_FP32, SCALE_POW2 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 BSCALE_BLOCK, BSCALE_TILE = 0, 1
+ACCUM_FP32, ACCUM_MFMA8 = 0, 1
 
 _lib = None
 
@@ -62,10 +63,10 @@ def lib():
         L.fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_blockscaled.restype = i32
         L.fp8_gemm_blockscaled.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32,
-                                           i64, i64, vp, i64, i32, vp, ctypes.c_size_t, vp]
+                                           i64, i64, vp, i64, i32, i32, vp, ctypes.c_size_t, vp]
         L.fp8_grouped_gemm.restype = i32
         L.fp8_grouped_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp, vp,
-                                       i64, i32, vp]
+                                       i64, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -144,7 +145,9 @@ def fp8_quant_block(w, scale_mode=SCALE_FP32, transpose=False, q=None, s=None, q
     if s is None:
         s = torch.empty(((rows + 127) // 128, cols // 128), dtype=torch.float32, device=w.device)
     if transpose and qt is None:
-        qt = torch.empty((cols, rows), dtype=torch.uint8, device=w.device)
+        # leading dimension padded to a multiple of 16 bytes, as the ABI requires
+        ld = (rows + 15) // 16 * 16
+        qt = torch.empty((cols, ld), dtype=torch.uint8, device=w.device)[:, :rows]
     _check(lib().fp8_quant_block(_ptr(w), rows, cols, _ld(w), int(scale_mode), _ptr(q), _ld(q),
                                  _ptr(qt) if transpose else None, _ld(qt) if transpose else 0,
                                  _ptr(s), _ld(s), _stream()), "fp8_quant_block")
@@ -158,7 +161,7 @@ def gemm_workspace_bytes(M, N, K):
 
 
 def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_BF16, d=None,
-                         workspace=None):
+                         workspace=None, accum=ACCUM_FP32):
     """D[m,n] = sum_g sa[g,m] * SB(n,g) * sum_{k in g} dec(a[m,k]) dec(b[n,k]).
     a [M, K] and b [N, K] uint8 codes; sa [K/128, >=M] fp32; sb fp32 read as
     SB(n,g) = sb[(n//128)*sb_s0 + g*sb_s1] (BLOCK) or sb[g*sb_s0 + n] (TILE)."""
@@ -179,13 +182,14 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().fp8_gemm_blockscaled(M, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa), _ptr(b), _ld(b),
                                       _ptr(sb), int(bscale_kind), int(sb_s0), int(sb_s1), _ptr(d),
-                                      _ld(d), int(out_dtype),
+                                      _ld(d), int(out_dtype), int(accum),
                                       _ptr(workspace) if workspace is not None else None, ws_bytes,
                                       _stream()), "fp8_gemm_blockscaled")
     return d
 
 
-def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None, d=None):
+def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None, d=None,
+                     accum=ACCUM_FP32):
     """Grouped block-scaled GEMM: rows offsets[e]..offsets[e+1]-1 of a use
     expert e's codes b[e] [N, K] and block scales sb[e] [N/128, K/128].
     offsets is an int32 device tensor; rows_bound defaults to a.shape[0]."""
@@ -202,24 +206,24 @@ def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None,
     if d is None:
         d = torch.empty((rows, N), dtype=dt, device=a.device)
     _check(lib().fp8_grouped_gemm(G, rows, N, K, _ptr(offsets), _ptr(a), _ld(a), _ptr(sa), _ld(sa),
-                                  _ptr(b), _ptr(sb), _ptr(d), _ld(d), int(out_dtype), _stream()),
+                                  _ptr(b), _ptr(sb), _ptr(d), _ld(d), int(out_dtype), int(accum), _stream()),
            "fp8_grouped_gemm")
     return d
 
 
 # ---- the three GEMMs of a Linear ---------------------------------------------------
 
-def linear_fprop(qx, sx, qw, sw, out_dtype=OUT_BF16):
+def linear_fprop(qx, sx, qw, sw, out_dtype=OUT_BF16, accum=ACCUM_FP32):
     """Y = X W^T from quant_tile(X, ROW) and quant_block(W)."""
-    return fp8_gemm_blockscaled(qx, sx, qw, sw, BSCALE_BLOCK, _ld(sw), 1, out_dtype)
+    return fp8_gemm_blockscaled(qx, sx, qw, sw, BSCALE_BLOCK, _ld(sw), 1, out_dtype, accum=accum)
 
 
-def linear_dgrad(qdy, sdy, qwt, sw, out_dtype=OUT_F32):
+def linear_dgrad(qdy, sdy, qwt, sw, out_dtype=OUT_F32, accum=ACCUM_FP32):
     """dX = dY W from quant_tile(dY, ROW) and the transposed codes qt of
     quant_block(W) (scales of W read transposed)."""
-    return fp8_gemm_blockscaled(qdy, sdy, qwt, sw, BSCALE_BLOCK, 1, _ld(sw), out_dtype)
+    return fp8_gemm_blockscaled(qdy, sdy, qwt, sw, BSCALE_BLOCK, 1, _ld(sw), out_dtype, accum=accum)
 
 
-def linear_wgrad(qdyt, sdyt, qxt, sxt, out_dtype=OUT_F32):
+def linear_wgrad(qdyt, sdyt, qxt, sxt, out_dtype=OUT_F32, accum=ACCUM_FP32):
     """dW = dY^T X from quant_tile(dY, COL) and quant_tile(X, COL)."""
-    return fp8_gemm_blockscaled(qdyt, sdyt, qxt, sxt, BSCALE_TILE, _ld(sxt), 0, out_dtype)
+    return fp8_gemm_blockscaled(qdyt, sdyt, qxt, sxt, BSCALE_TILE, _ld(sxt), 0, out_dtype, accum=accum)

@@ -134,9 +134,10 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
 FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                                       const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
                                       const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1, void* d,
-                                      int64_t ldd, int out_dtype, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      int64_t ldd, int out_dtype, int accum, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
     if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8) return FP8BS_ERR_ARG;
     if (int r = check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
     if (M == 0 || N == 0) return FP8BS_OK;
     const size_t need = fp8_gemm_workspace_bytes(M, N, K);
@@ -160,6 +161,7 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
     g.d = d;
     g.ldd = ldd;
     g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.accum = accum;
     g.splits = need > 0 ? fp8bs::gemm_splits(M, N, K) : 1;
     g.ws = (float*)workspace;
     g.ws_ld = (N + 3) / 4 * 4;
@@ -168,8 +170,10 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
 
 FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K, const int32_t* offsets,
                                   const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
-                                  const float* sb, void* d, int64_t ldd, int out_dtype, void* stream) {
+                                  const float* sb, void* d, int64_t ldd, int out_dtype, int accum,
+                                  void* stream) {
     if (G < 0 || rows_bound < 0) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8) return FP8BS_ERR_ARG;
     if (G > 0 && !offsets) return FP8BS_ERR_ARG;
     if (N % 128 != 0) return FP8BS_ERR_SHAPE;
     if (int r = check_gemm_common(rows_bound, N, K, a, lda, sa, ldsa, b, K, sb, d, ldd, out_dtype)) return r;
@@ -191,6 +195,7 @@ FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t 
     g.d = d;
     g.ldd = ldd;
     g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.accum = accum;
     g.splits = 1;
     g.offsets = offsets;
     g.G = G;

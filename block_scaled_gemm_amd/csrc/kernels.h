@@ -35,6 +35,7 @@ struct GemmArgs {
     void* d;
     int64_t ldd;
     int out_f32;  // 0 bf16, 1 fp32
+    int accum;    // 0 FP32-accurate group partials (f16 matrix cores), 1 FP8 matrix cores
     // split-K (dense only): partials in `ws`, row stride ws_ld floats
     float* ws;
     int splits;

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 1
+#define FP8BS_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -82,6 +82,18 @@ enum {
 
 /* GEMM output type. */
 enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_F32 = 1 };
+
+/* How each 128-element group partial is formed before its FP32 promotion.
+ *  FP8BS_ACCUM_FP32:  products exact and summed at FP32 accuracy.  The E4M3
+ *    operands are widened exactly to f16 and multiplied on the f16 matrix
+ *    cores (half the FP8 matrix-core rate).
+ *  FP8BS_ACCUM_MFMA8: the FP8 matrix cores' own sum of the group (full FP8
+ *    rate).  On gfx950 that sum is not FP32-accurate: it loses up to about
+ *    2^-12 of the largest product in the instruction -- the same limited
+ *    accumulation the pages report for their tensor cores.  Contract:
+ *    |D - exact| <= 2^-10 * sum_g |sa*SB| * sum_k |dec(a)*dec(b)|, plus the
+ *    output rounding. */
+enum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_MFMA8 = 1 };
 
 /* How the B operand's scales are addressed (SB(n, g) for column n of the
  * output and K group g). */
@@ -167,9 +179,9 @@ int fp8_quant_block(const uint16_t *w, int64_t rows, int64_t cols,
  *   D[m][n] = sum_{g < K/128} sa[g*ldsa + m] * SB(n, g) *
  *             sum_{k = 128g}^{128g+127} dec(a[m*lda + k]) * dec(b[n*ldb + k])
  *
- * Each group's inner sum is formed on the matrix cores and multiplied by its
- * two scales into an FP32 accumulator, which is rounded once to the output
- * type (bf16: round to nearest even).
+ * Each group's inner sum is formed on the matrix cores (see FP8BS_ACCUM_*)
+ * and multiplied by its two scales into an FP32 accumulator, which is
+ * rounded once to the output type (bf16: round to nearest even).
  *   a      E4M3 codes [M][lda], K contiguous.
  *   sa     per-row scale of each K group of a: sa[g*ldsa + m].
  *   b      E4M3 codes [N][ldb], K contiguous ("TN": both operands K-major).
@@ -178,6 +190,7 @@ int fp8_quant_block(const uint16_t *w, int64_t rows, int64_t cols,
  *          Dgrad (B = qt of W, its scales transposed): BLOCK, s0 = 1, s1 = lds.
  *          Wgrad (B from fp8_quant_tile COL):          TILE,  s0 = lds.
  *   d      output [M][ldd], bf16 bits (FP8BS_OUT_BF16) or fp32 (FP8BS_OUT_F32).
+ *   accum  FP8BS_ACCUM_FP32 or FP8BS_ACCUM_MFMA8.
  *   workspace  device scratch of at least fp8_gemm_workspace_bytes(M, N, K)
  *          bytes (may be NULL when that is 0); it holds split-K partials
  *          when K is long and the output small.  The reduction over splits
@@ -193,8 +206,9 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t *a,
                          int64_t lda, const float *sa, int64_t ldsa,
                          const uint8_t *b, int64_t ldb, const float *sb,
                          int bscale_kind, int64_t sb_s0, int64_t sb_s1,
-                         void *d, int64_t ldd, int out_dtype, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         void *d, int64_t ldd, int out_dtype, int accum,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /* Workspace bytes fp8_gemm_blockscaled needs for this shape (0 = none). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -218,6 +232,7 @@ size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *            (fp8_quant_tile ROW of the rows gathered per expert).
  *   b        codes [G][N][K] (contiguous), sb  block scales [G][N/128][K/128].
  *   d        output [rows][ldd], bf16 or fp32 as out_dtype.
+ *   accum    FP8BS_ACCUM_FP32 or FP8BS_ACCUM_MFMA8, as for the dense GEMM.
  * N and K must be multiples of 128.  Alignment as fp8_gemm_blockscaled;
  * ldsa >= rows_bound.
  * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
@@ -226,7 +241,7 @@ int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K,
                      const int32_t *offsets, const uint8_t *a, int64_t lda,
                      const float *sa, int64_t ldsa, const uint8_t *b,
                      const float *sb, void *d, int64_t ldd, int out_dtype,
-                     void *stream);
+                     int accum, void *stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bs.abi_version() == 1
+    assert bs.abi_version() == 2
     for s in range(7):
         assert bs.status_string(s)
     assert "unknown" in bs.status_string(99)
@@ -87,15 +87,15 @@ def test_quant_block_validation(kw, want):
 
 def _gemm(**kw):
     a = dict(M=256, N=256, K=512, a=FAKE, lda=512, sa=FAKE, ldsa=256, b=FAKE, ldb=512, sb=FAKE,
-             kind=0, s0=4, s1=1, d=FAKE, ldd=256, out=0, ws=None, wsb=0)
+             kind=0, s0=4, s1=1, d=FAKE, ldd=256, out=0, acc=0, ws=None, wsb=0)
     a.update(kw)
     return bs.lib().fp8_gemm_blockscaled(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["ldsa"],
                                          a["b"], a["ldb"], a["sb"], a["kind"], a["s0"], a["s1"], a["d"],
-                                         a["ldd"], a["out"], a["ws"], a["wsb"], None)
+                                         a["ldd"], a["out"], a["acc"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
+    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(acc=2), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
     (dict(M=-1), ARG), (dict(lda=256), ARG), (dict(ldd=128), ARG), (dict(ldsa=100), ARG),
     (dict(K=500, lda=512, ldb=512), SHAPE), (dict(a=FAKE + 8), ALIGN), (dict(d=FAKE + 4), ALIGN),
     (dict(lda=520), ALIGN), (dict(ldd=258), ALIGN), (dict(sa=FAKE + 1), ALIGN),
@@ -115,15 +115,15 @@ def test_workspace_query():
 
 def _grouped(**kw):
     a = dict(G=4, rows=512, N=256, K=512, off=FAKE, a=FAKE, lda=512, sa=FAKE, ldsa=512, b=FAKE,
-             sb=FAKE, d=FAKE, ldd=256, out=0)
+             sb=FAKE, d=FAKE, ldd=256, out=0, acc=0)
     a.update(kw)
     return bs.lib().fp8_grouped_gemm(a["G"], a["rows"], a["N"], a["K"], a["off"], a["a"], a["lda"],
                                      a["sa"], a["ldsa"], a["b"], a["sb"], a["d"], a["ldd"], a["out"],
-                                     None)
+                                     a["acc"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(G=-1), ARG), (dict(off=None), ARG), (dict(N=200, ldd=256), SHAPE),
+    (dict(G=-1), ARG), (dict(acc=-1), ARG), (dict(off=None), ARG), (dict(N=200, ldd=256), SHAPE),
     (dict(K=500, lda=512), SHAPE), (dict(ldsa=100), ARG), (dict(off=FAKE + 2), ALIGN),
     (dict(G=0), OK), (dict(rows=0), OK),
 ])

@@ -2,8 +2,13 @@
 
 The inputs are quantised on the GPU (codes and scales checked bit-exact
 against the oracle's), then the GPU GEMM is compared with the oracle's
-exact-group-partial FP64 result under the max relative error with a 1%-of-max
-floor: <= 1e-3 for fp32 output, <= 8e-3 for bf16 output."""
+exact-group-partial FP64 result.
+
+Default accumulation (FP32-accurate group partials): max relative error with
+a 1%-of-max floor <= 1e-3 for fp32 output, <= 8e-3 for bf16 output.
+FP8-matrix-core accumulation: the documented bound
+|D - R| <= 2^-10 * Rabs + output rounding, where Rabs is the same GEMM on
+the absolute values (sign bits cleared, scales are positive)."""
 import numpy as np
 import pytest
 import torch
@@ -14,12 +19,31 @@ from gpu_util import workload, bf16_f64, dev, dev_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 
-TOL = {0: 8e-3, 1: 1e-3}  # out_dtype -> gate
+TOL = {0: 8e-3, 1: 1e-3}  # out_dtype -> gate for the default accumulation
+ACCUMS = pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
 
 
 def out_f64(t):
     h = host(t)
     return bf16_f64(h) if h.dtype == np.uint16 else h.astype(np.float64)
+
+
+def check(y, r, rabs, out, accum, groups, tag):
+    """Gate y (float64 values of the GPU output) against the oracle r."""
+    err = oracle.max_rel_err(y, r)
+    if accum == 0:
+        log(f"{tag}: max rel err {err:.3e} (gate {TOL[out]:.0e})")
+        assert err <= TOL[out], (tag, err)
+    else:
+        rnd = 2.0 ** -8 * np.abs(r) if out == 0 else 2.0 ** -23 * np.abs(r)
+        bound = 2.0 ** -10 * rabs + groups * 2.0 ** -23 * rabs + rnd + 1e-30
+        ratio = float(np.max(np.abs(y - r) / bound))
+        log(f"{tag}: max rel err {err:.3e}; error / bound {ratio:.3f}")
+        assert ratio <= 1.0, (tag, ratio)
+
+
+def absolute(codes):
+    return codes & np.uint8(0x7F)
 
 
 def quant_both(hip, orc, x, kind, mode):
@@ -42,53 +66,62 @@ def quant_both(hip, orc, x, kind, mode):
     return q, s, qt, wq, ws, wqt
 
 
+def full(orc, a, sa, b, sb, kind, s0, s1):
+    """Oracle result and its absolute-value companion."""
+    return (orc.gemm(a, sa, b, sb, kind, s0, s1),
+            orc.gemm(absolute(a), sa, absolute(b), sb, kind, s0, s1))
+
+
+def sampled(orc, a, sa, b, sb, kind, s0, s1, mi, ni):
+    return (orc.gemm_entries(a, sa, b, sb, kind, s0, s1, mi, ni),
+            orc.gemm_entries(absolute(a), sa, absolute(b), sb, kind, s0, s1, mi, ni))
+
+
+@ACCUMS
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
-def test_tiny_fprop(hip, orc, out):
+def test_tiny_fprop(hip, orc, out, accum):
     """Workload 0 in full: X[128x512] 1x128 tiles, W[256x512] 128x128 blocks."""
     d = workload("tiny_fprop")
     qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, d["X"], "row", 0)
     qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, d["W"], "block", 0)
-    y = hip.linear_fprop(qx, sx, qw, sw, out)
-    r = orc.gemm(wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
-    err = oracle.max_rel_err(out_f64(y), r)
-    log(f"tiny fprop out={out} err={err:.3e}")
-    assert err <= TOL[out]
+    y = hip.linear_fprop(qx, sx, qw, sw, out, accum=accum)
+    r, rabs = full(orc, wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
+    check(out_f64(y), r, rabs, out, accum, 4, f"tiny fprop out={out} accum={accum}")
 
 
+@ACCUMS
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
-def test_linear_three_gemms_ragged(hip, orc, mode, out):
-    """Fprop, Dgrad and Wgrad at a size spanning several tiles with ragged
-    M and N tails: X[300x1024], W[260x1024], dY[384x260] (tokens 384)."""
+def test_linear_three_gemms_ragged(hip, orc, mode, out, accum):
+    """Fprop, Dgrad and Wgrad at sizes spanning several tiles with ragged
+    tails: Fprop X[300x1024] W[260x1024]; Dgrad dY[384x256] W[256x1024];
+    Wgrad dY^T X2 with 384 tokens, X2[384x200]."""
     X = inputs.random_bf16(101, (300, 1024))
     W = inputs.random_bf16(102, (260, 1024), sd=0.02, outliers=False)
-    # Fprop Y = X W^T
     qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, X, "row", mode)
-    qw, sw, qwt, wqw, wsw, wqwt = quant_both(hip, orc, W, "block", mode)
-    y = hip.linear_fprop(qx, sx, qw, sw, out)
-    r = orc.gemm(wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
-    e1 = oracle.max_rel_err(out_f64(y), r)
-    # Dgrad dX = dY W: A = dY [384 x 260] is K-ragged for 128 groups -> pad tokens of
-    # W to a multiple of 128 is not allowed; use W rows = 256 for this GEMM
+    qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, W, "block", mode)
+    y = hip.linear_fprop(qx, sx, qw, sw, out, accum=accum)
+    r, rabs = full(orc, wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
+    check(out_f64(y), r, rabs, out, accum, 8, f"ragged fprop mode={mode} out={out} accum={accum}")
+    # Dgrad: the contraction runs over W's 256 rows (a multiple of 128)
     Wd = W[:256]
     dY = inputs.random_bf16(103, (384, 256), sd=1e-3)
     qd, sd_, _, wqd, wsd, _ = quant_both(hip, orc, dY, "row", mode)
     qwd, swd, qwdt, wqwd, wswd, wqwdt = quant_both(hip, orc, Wd, "block", mode)
-    dx = hip.linear_dgrad(qd, sd_, qwdt, swd, out)
-    r2 = orc.gemm(wqd, wsd, wqwdt, wswd, 0, 1, wswd.shape[1])
-    e2 = oracle.max_rel_err(out_f64(dx), r2)
-    # Wgrad dW = dY^T X2 with tokens 384: A = dY^T (COL), B = X2^T (COL)
+    dx = hip.linear_dgrad(qd, sd_, qwdt, swd, out, accum=accum)
+    r, rabs = full(orc, wqd, wsd, wqwdt, wswd, 0, 1, wswd.shape[1])
+    check(out_f64(dx), r, rabs, out, accum, 2, f"ragged dgrad mode={mode} out={out} accum={accum}")
+    # Wgrad: A = dY^T (128x1 tiles along tokens), B = X2^T (same)
     X2 = inputs.random_bf16(104, (384, 200))
     qdt, sdt, _, wqdt, wsdt, _ = quant_both(hip, orc, dY, "col", mode)
     qxt, sxt, _, wqxt, wsxt, _ = quant_both(hip, orc, X2, "col", mode)
-    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, out)
-    r3 = orc.gemm(wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
-    e3 = oracle.max_rel_err(out_f64(dw), r3)
-    log(f"ragged linear mode={mode} out={out}: fprop {e1:.2e} dgrad {e2:.2e} wgrad {e3:.2e}")
-    assert max(e1, e2, e3) <= TOL[out]
+    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, out, accum=accum)
+    r, rabs = full(orc, wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
+    check(out_f64(dw), r, rabs, out, accum, 3, f"ragged wgrad mode={mode} out={out} accum={accum}")
 
 
-def test_exact_special_cases(hip, orc):
+@ACCUMS
+def test_exact_special_cases(hip, orc, accum):
     """Bit-exact GPU results where the arithmetic is exact: A = identity with
     power-of-two block scales gives the dequantised B^T; small integers with
     unit scales give the integer product."""
@@ -101,7 +134,7 @@ def test_exact_special_cases(hip, orc):
     sa = np.ones((K // 128, K), np.float32)
     b = rng.choice(finite, (N, K))
     sbk = (2.0 ** rng.integers(-20, 20, (N // 128, K // 128))).astype(np.float32)
-    y = hip.fp8_gemm_blockscaled(dev(a), dev(sa), dev(b), dev(sbk), 0, sbk.shape[1], 1, 1)
+    y = hip.fp8_gemm_blockscaled(dev(a), dev(sa), dev(b), dev(sbk), 0, sbk.shape[1], 1, 1, accum=accum)
     np.testing.assert_array_equal(out_f64(y), orc.gemm(a, sa, b, sbk, 0, sbk.shape[1], 1))
     ints = {int(v): c for c, v in enumerate(table) if not np.isnan(v) and v == int(v) and abs(v) <= 8 and c != 0x80}
     keys = np.array(sorted(ints))
@@ -110,11 +143,12 @@ def test_exact_special_cases(hip, orc):
     ca = np.vectorize(ints.get)(ia).astype(np.uint8)
     cb = np.vectorize(ints.get)(ib).astype(np.uint8)
     y = hip.fp8_gemm_blockscaled(dev(ca), dev(np.ones((K // 128, M), np.float32)), dev(cb),
-                                 dev(np.ones((2, K // 128), np.float32)), 0, K // 128, 1, 1)
+                                 dev(np.ones((2, K // 128), np.float32)), 0, K // 128, 1, 1, accum=accum)
     np.testing.assert_array_equal(out_f64(y), (ia @ ib.T).astype(np.float64))
 
 
-def test_empty_k_and_deterministic(hip, orc):
+@ACCUMS
+def test_empty_k_and_deterministic(hip, orc, accum):
     """K = 0 writes zeros; repeated calls are bitwise identical."""
     M, N = 130, 140
     a = torch.zeros((M, 0), dtype=torch.uint8, device="cuda")
@@ -122,33 +156,32 @@ def test_empty_k_and_deterministic(hip, orc):
     sa = torch.zeros((1, M), dtype=torch.float32, device="cuda")
     sb = torch.zeros((2, 1), dtype=torch.float32, device="cuda")
     d = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
-    hip.fp8_gemm_blockscaled(a, sa, b, sb, 0, 1, 1, 1, d=d)
+    hip.fp8_gemm_blockscaled(a, sa, b, sb, 0, 1, 1, 1, d=d, accum=accum)
     assert torch.count_nonzero(d).item() == 0
     X = inputs.random_bf16(9, (512, 2048))
     W = inputs.random_bf16(10, (384, 2048), sd=0.02, outliers=False)
     qx, sx = hip.fp8_quant_tile(dev_bf16(X))
     qw, sw, _ = hip.fp8_quant_block(dev_bf16(W))
-    y1 = hip.linear_fprop(qx, sx, qw, sw, 1)
-    y2 = hip.linear_fprop(qx, sx, qw, sw, 1)
+    y1 = hip.linear_fprop(qx, sx, qw, sw, 1, accum=accum)
+    y2 = hip.linear_fprop(qx, sx, qw, sw, 1, accum=accum)
     assert torch.equal(y1, y2)
 
 
+@ACCUMS
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
-def test_large_k_split(hip, orc, mode):
+def test_large_k_split(hip, orc, mode, accum):
     """256x256x65536 with U(-1,1) inputs (workload 4b): split-K partials
-    reduced in a fixed order; fp32 output within 1e-3 of the exact result,
-    and bitwise repeatable."""
+    reduced in a fixed order, fp32 output, bitwise repeatable."""
     d = workload("large_k")
     qa, sa, _, wqa, wsa, _ = quant_both(hip, orc, d["A"], "row", mode)
     qb, sb, _, wqb, wsb, _ = quant_both(hip, orc, d["B"], "block", mode)
     assert hip.gemm_workspace_bytes(256, 256, 65536) > 0
-    y = hip.linear_fprop(qa, sa, qb, sb, 1)
-    y2 = hip.linear_fprop(qa, sa, qb, sb, 1)
+    y = hip.linear_fprop(qa, sa, qb, sb, 1, accum=accum)
+    y2 = hip.linear_fprop(qa, sa, qb, sb, 1, accum=accum)
     assert torch.equal(y, y2)
-    r = orc.gemm(wqa, wsa, wqb, wsb, 0, wsb.shape[1], 1)
-    err = oracle.max_rel_err(out_f64(y), r)
-    log(f"large K mode={mode}: max rel err {err:.3e}, normwise {oracle.normwise_err(out_f64(y), r):.3e}")
-    assert err <= 1e-3
+    r, rabs = full(orc, wqa, wsa, wqb, wsb, 0, wsb.shape[1], 1)
+    log(f"large K mode={mode} accum={accum}: normwise {oracle.normwise_err(out_f64(y), r):.3e}")
+    check(out_f64(y), r, rabs, 1, accum, 512, f"large K mode={mode} accum={accum}")
 
 
 def _sampled(rng, M, N, count=3000):
@@ -162,37 +195,34 @@ def _sampled(rng, M, N, count=3000):
     return mi, ni
 
 
-def test_dense_fprop_full_size(hip, orc):
+@ACCUMS
+def test_dense_fprop_full_size(hip, orc, accum):
     """Workload 1 at its real size (4096 x 18432 x 7168, bf16 out) in the
     launch configuration the benchmark times; outputs sampled."""
     d = workload("dense_fprop")
     qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, d["X"], "row", 0)
     qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, d["W"], "block", 0)
-    y = hip.linear_fprop(qx, sx, qw, sw, 0)
+    y = hip.linear_fprop(qx, sx, qw, sw, 0, accum=accum)
     mi, ni = _sampled(np.random.default_rng(1), 4096, 18432)
-    r = orc.gemm_entries(wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1, mi, ni)
-    yh = out_f64(y)[mi, ni]
-    err = oracle.max_rel_err(yh, r)
-    log(f"dense fprop full size: sampled max rel err {err:.3e}")
-    assert err <= TOL[0]
+    r, rabs = sampled(orc, wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1, mi, ni)
+    check(out_f64(y)[mi, ni], r, rabs, 0, accum, 56, f"dense fprop full size accum={accum}")
 
 
-def test_expert_backward_full_size(hip, orc):
+@ACCUMS
+def test_expert_backward_full_size(hip, orc, accum):
     """Workload 2 at its real size: Dgrad 8192x7168x2048 and Wgrad
     2048x7168x8192, fp32 out; outputs sampled."""
     d = workload("expert_backward")
     qd, sd_, _, wqd, wsd, _ = quant_both(hip, orc, d["dY"], "row", 0)
     qw, sw, qwt, wqw, wsw, wqwt = quant_both(hip, orc, d["W"], "block", 0)
-    dx = hip.linear_dgrad(qd, sd_, qwt, sw, 1)
+    dx = hip.linear_dgrad(qd, sd_, qwt, sw, 1, accum=accum)
     mi, ni = _sampled(np.random.default_rng(2), 8192, 7168)
-    r = orc.gemm_entries(wqd, wsd, wqwt, wsw, 0, 1, wsw.shape[1], mi, ni)
-    e1 = oracle.max_rel_err(out_f64(dx)[mi, ni], r)
+    r, rabs = sampled(orc, wqd, wsd, wqwt, wsw, 0, 1, wsw.shape[1], mi, ni)
+    check(out_f64(dx)[mi, ni], r, rabs, 1, accum, 16, f"expert dgrad full size accum={accum}")
     del dx
     qdt, sdt, _, wqdt, wsdt, _ = quant_both(hip, orc, d["dY"], "col", 0)
     qxt, sxt, _, wqxt, wsxt, _ = quant_both(hip, orc, d["X"], "col", 0)
-    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, 1)
+    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, 1, accum=accum)
     mi, ni = _sampled(np.random.default_rng(3), 2048, 7168)
-    r = orc.gemm_entries(wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0, mi, ni)
-    e2 = oracle.max_rel_err(out_f64(dw)[mi, ni], r)
-    log(f"expert backward full size: dgrad {e1:.3e} wgrad {e2:.3e}")
-    assert max(e1, e2) <= TOL[1]
+    r, rabs = sampled(orc, wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0, mi, ni)
+    check(out_f64(dw)[mi, ni], r, rabs, 1, accum, 64, f"expert wgrad full size accum={accum}")

@@ -8,6 +8,21 @@ from block_scaled_gemm_amd import inputs
 from gpu_util import workload, bf16_f64, dev, dev_bf16, host, log
 
 pytestmark = pytest.mark.gpu
+ACCUMS = pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
+
+
+def check(y, r, rabs, out, accum, groups, tag):
+    err = oracle.max_rel_err(y, r)
+    if accum == 0:
+        tol = 1e-3 if out == 1 else 8e-3
+        log(f"{tag}: max rel err {err:.3e} (gate {tol:.0e})")
+        assert err <= tol, (tag, err)
+    else:
+        rnd = 2.0 ** -8 * np.abs(r) if out == 0 else 2.0 ** -23 * np.abs(r)
+        bound = 2.0 ** -10 * rabs + groups * 2.0 ** -23 * rabs + rnd + 1e-30
+        ratio = float(np.max(np.abs(y - r) / bound))
+        log(f"{tag}: max rel err {err:.3e}; error / bound {ratio:.3f}")
+        assert ratio <= 1.0, (tag, ratio)
 
 
 def out_f64(t):
@@ -29,8 +44,9 @@ def quant_experts(hip, orc, Xcat, W, mode):
             wqx, wsx, wqw.reshape(G, N, K), wsw.reshape(G, N // 128, K // 128))
 
 
+@ACCUMS
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
-def test_grouped_small_with_empty_experts(hip, orc, out):
+def test_grouped_small_with_empty_experts(hip, orc, out, accum):
     """6 experts with 0, 1, 130, 0, 257 and 40 rows (empty experts, a single
     row, ragged tiles), N = 256, K = 512, power-of-two scales."""
     counts = [0, 1, 130, 0, 257, 40]
@@ -39,14 +55,13 @@ def test_grouped_small_with_empty_experts(hip, orc, out):
     Xcat = inputs.random_bf16(201, (int(offsets[-1]), 512))
     W = inputs.random_bf16(202, (len(counts), 256, 512), sd=0.02, outliers=False)
     qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
-    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, out)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, out, accum=accum)
     r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
-    tol = 1e-3 if out == 1 else 8e-3
+    rabs = orc.grouped_gemm(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw)
     for e in range(len(counts)):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
-            err = oracle.max_rel_err(out_f64(y)[r0:r1], r[r0:r1])
-            assert err <= tol, (e, err)
+            check(out_f64(y)[r0:r1], r[r0:r1], rabs[r0:r1], out, accum, 4, f"expert {e} out={out} accum={accum}")
 
 
 def test_grouped_rows_beyond_offsets_untouched(hip, orc):
@@ -61,10 +76,10 @@ def test_grouped_rows_beyond_offsets_untouched(hip, orc):
     assert torch.all(d[160:] == 3.0).item()
 
 
-def _check_sampled(hip, orc, data, mode, tag):
+def _check_sampled(hip, orc, data, mode, tag, accum):
     Xcat, W, offsets = data["Xcat"], data["W"], data["offsets"]
     qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, mode)
-    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 0)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 0, accum=accum)
     rows, N = y.shape
     rng = np.random.default_rng(7)
     mi = rng.integers(0, rows, 3000)
@@ -75,17 +90,18 @@ def _check_sampled(hip, orc, data, mode, tag):
     mi = np.concatenate([mi, starts, ends])
     ni = np.concatenate([ni, rng.integers(0, N, starts.size + ends.size)])
     r = orc.grouped_gemm_entries(offsets, wqx, wsx, wqw, wsw, mi, ni)
-    err = oracle.max_rel_err(out_f64(y)[mi, ni], r)
-    log(f"{tag}: sampled max rel err {err:.3e}")
-    assert err <= 8e-3
+    rabs = orc.grouped_gemm_entries(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw, mi, ni)
+    check(out_f64(y)[mi, ni], r, rabs, 0, accum, wqw.shape[2] // 128, f"{tag} accum={accum}")
 
 
-def test_grouped_upproj_full_size(hip, orc):
+@ACCUMS
+def test_grouped_upproj_full_size(hip, orc, accum):
     """Workload 3: 32 local experts of a top-8-of-256 routing of 4096
     tokens, N = 4096, K = 7168, power-of-two scales, bf16 out."""
-    _check_sampled(hip, orc, workload("grouped_upproj"), 1, "grouped up-proj")
+    _check_sampled(hip, orc, workload("grouped_upproj"), 1, "grouped up-proj", accum)
 
 
-def test_decode_grouped_full_size(hip, orc):
+@ACCUMS
+def test_decode_grouped_full_size(hip, orc, accum):
     """Workload 4a: 64 experts with 1..256 rows each, N = 2048, K = 7168."""
-    _check_sampled(hip, orc, workload("decode_grouped"), 0, "decode grouped")
+    _check_sampled(hip, orc, workload("decode_grouped"), 0, "decode grouped", accum)

@@ -16,7 +16,7 @@ def test_cast_all_fp32_patterns(hip, orc):
     chunk = 1 << 27
     bad = 0
     for start in range(0, 1 << 32, chunk):
-        u = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        u = np.arange(start, start + chunk, dtype=np.uint32)
         f = u.view(np.float32)
         got = host(hip.fp8_cast_e4m3(dev(f)))
         want = orc.encode(f)
