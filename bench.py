@@ -65,13 +65,13 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(X, W, target_s=10.0):
+def cpu_baseline(X, W, target_s=20.0):
     """Time the CPU oracle on a sub-block of the workload: quantise X rows
     [0, ms) and W rows [0, ns), then their GEMM; grow ns until the run takes
     about target_s.  Returns the baseline dict."""
     import oracle
     orc = oracle.default()
-    ms, ns = 128, 256
+    ms, ns = 16, 1024
     while True:
         x, w = X[:ms], W[:ns]
         t0 = time.perf_counter()
@@ -79,10 +79,13 @@ def cpu_baseline(X, W, target_s=10.0):
         qw, sw, _ = orc.quant_block(w, 0)
         orc.gemm(qx, sx, qw, sw, 0, sw.shape[1], 1)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or ns >= N:
+        if dt >= target_s / 3 or (ms >= M and ns >= N):
             break
-        ns = min(N, ns * max(2, int(target_s / max(dt, 1e-3))))
-        ns = (ns + 127) // 128 * 128
+        grow = max(2.0, min(64.0, target_s / max(dt, 1e-3)))
+        if ns < N:
+            ns = min(N, (int(ns * grow) + 127) // 128 * 128)
+        else:
+            ms = min(M, int(ms * grow))
     flops = 2.0 * ms * ns * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
             "kind": "oracle",

@@ -8,32 +8,40 @@
 //
 // Two ways of forming P_g (the `accum` argument):
 //
-//  ACC_F32 (default).  The gfx950 FP8 matrix cores do not add their products
-//  at FP32 accuracy: on crafted inputs every FP8 MFMA form loses about 2^-12
-//  of the largest product inside one instruction -- the limited accumulation
-//  the pages measure on their own tensor cores.  This path therefore widens
-//  the E4M3 tiles exactly to f16 while staging them into LDS
+//  ACC_F32 (0, default).  The gfx950 FP8 matrix cores do not add their
+//  products at FP32 accuracy: on crafted inputs every FP8 MFMA form loses
+//  about 2^-12 of the largest product inside one instruction -- the limited
+//  accumulation the pages measure on their own tensor cores.  This path
+//  widens each E4M3 fragment exactly to f16 right after reading it from LDS
 //  (v_cvt_scalef32_pk_f16_fp8 with scale 1 is exact for every finite code)
 //  and forms P_g with v_mfma_f32_32x32x16_f16, whose products are exact and
-//  whose sums are FP32-accurate.  Tiles 128x128 per 256-thread workgroup,
-//  64x64 per wave as 2x2 sub-tiles of 32x32, 8 MFMAs per sub-tile per group.
+//  whose sums are FP32-accurate.  Workgroup tile 256 (m) x 128 (n); 8 waves
+//  of 64x64, each 2x2 sub-tiles of 32x32, 8 MFMAs per sub-tile per group.
 //
-//  ACC_MFMA8.  P_g straight from v_mfma_f32_16x16x128_f8f6f4 (one MFMA = one
-//  K group for a 16x16 sub-tile), at twice the matrix-core rate, with the
-//  matrix core's own limited accumulation inside the group.  Tiles 128x128,
-//  64x64 per wave as 4x4 sub-tiles of 16x16.
+//  ACC_MFMA8 (1).  P_g straight from v_mfma_f32_16x16x128_f8f6f4 (one MFMA
+//  is one K group of a 16x16 sub-tile) at twice the matrix-core rate, with
+//  the matrix core's own limited accumulation inside the group.  Workgroup
+//  tile 256 (m) x 128 (n); 8 waves of 64x64, 4x4 sub-tiles of 16x16.
 //
 // Both: the MFMA's first operand is the B (weight) tile and its second the
 // A (activation) tile, so each result sub-tile is D^T and every lane ends
 // with runs of four consecutive output columns of one row (one 8-byte bf16
-// or 16-byte fp32 store) and needs a single activation scale per sub-tile.
-// Both operands feed each lane the same k positions, so whatever order the
-// hardware pairs elements in, it pairs equal k.
+// or 16-byte fp32 store) and needs one activation scale per sub-tile.  Each
+// lane's k positions depend only on its lane index, identically for both
+// operands, so whatever order the hardware pairs elements in, equal k meet.
 //
-// Each K group of both tiles is staged global -> registers -> LDS, double-
-// buffered (the next group's loads are in flight while the current one is
-// multiplied), rows XOR-swizzled in 16-byte chunks so fragment reads of
-// consecutive rows hit distinct banks.
+// Staging: 512 threads (two waves per SIMD).  Each K group of both tiles
+// goes global -> LDS with global_load_lds_dwordx4 (no register staging:
+// lane i of a wave instruction lands at LDS base + 16*i, so each
+// instruction fills 8 rows of 128 B), the group's scales with 4-byte
+// global_load_lds (see dma16).  Tiles sit in LDS as FP8 codes, rows of 128 B whose
+// 16-byte chunks are XOR-swizzled by (row ^ row>>3) & 7 -- lanes fetch the
+// permuted chunk of their row, so coalescing is unchanged and the fragment
+// reads of 8 or 16 consecutive rows hit distinct banks.  STAGES groups are
+// in flight; one barrier per group both publishes the landed group and
+// frees the stage the next issue overwrites.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -45,8 +53,75 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;
-constexpr int BN = 128;
+constexpr int THREADS = 512;
+constexpr int WAVES = THREADS / 64;
+
+template <int ACC>
+struct Cfg;
+template <>
+struct Cfg<0> {  // f16 matrix cores
+    static constexpr int BM = 256, BN = 128;
+    static constexpr int WGM = 4, WGN = 2;  // wave grid (m, n): waves of 64 x 64
+    static constexpr int STAGES = 3;
+};
+template <>
+struct Cfg<1> {  // FP8 matrix cores
+    static constexpr int BM = 256, BN = 128;
+    static constexpr int WGM = 4, WGN = 2;  // waves of 64 x 64
+    static constexpr int STAGES = 3;
+};
+
+// LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
+// B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
+template <int ACC>
+struct Lds {
+    static constexpr int BM = Cfg<ACC>::BM, BN = Cfg<ACC>::BN;
+    static constexpr int A = 0;
+    static constexpr int B = BM * 128;
+    static constexpr int SA = B + BN * 128;
+    static constexpr int SB = SA + BM * 4;
+    static constexpr int STAGE = SB + BN * 4;
+    static constexpr int BYTES = STAGE * Cfg<ACC>::STAGES;
+};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global -> LDS loads.  Issued from inline assembly so that the
+// compiler does not treat the in-flight transfer as aliasing every later LDS
+// read (it would otherwise wait for all outstanding transfers, including the
+// prefetched groups, before the first read of the current group); the
+// kernel orders them itself with wait_and_barrier.  The instructions have
+// no register results.  M0 holds the wave-uniform LDS base; lane i's data
+// lands at M0 + size*i.  M0 is a reserved register the compiler never
+// assigns in these kernels, so it is not listed as clobbered.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gptr) : "memory");
+}
+
+// Wait until at most N of this wave's direct loads are in flight, then
+// barrier.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier();
+template <>
+__device__ __forceinline__ void wait_and_barrier<0>() {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <>
+__device__ __forceinline__ void wait_and_barrier<6>() {
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int f8_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 // ---- tile description and workgroup -> tile order ---------------------------------
 
@@ -84,176 +159,195 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
     tn = r / gm;
 }
 
-// ---- staging: one K group of both tiles, global -> registers ----------------------------
-//
-// 1024 16-byte chunks per 128x128 FP8 tile: thread t takes chunks t + 256j,
-// i.e. row (t + 256j) / 8 and k-chunk t % 8, so 8 lanes cover a 128-byte row.
+// ---- staging: issue one K group of both tiles and their scales into a stage ---------------
 
-struct Stage {
-    uint4 a[4];
-    uint4 b[4];
-    float s;    // sa of row t (t < 128) or, for tile-kind B scales, sb of column t-128
-    float sbk;  // block-kind B scale of this group (uniform)
-};
-
-template <int KIND>
-__device__ __forceinline__ void load_stage(Stage& st, const Tile& T, int64_t g, int t) {
+template <int ACC, int KIND>
+__device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* stage, int wave, int lane) {
+    constexpr int BM = Cfg<ACC>::BM, BN = Cfg<ACC>::BN;
     const int64_t k0 = g * 128;
+    // A: BM/8 instructions of 8 rows, spread over the waves
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int cid = t + 256 * j;
-        const int row = cid >> 3, kc = cid & 7;
-        int64_t ma = T.m0 + row;
-        ma = ma < T.m_end ? ma : T.m_end - 1;
-        int64_t nb = T.n0 + row;
-        nb = nb < T.n_end ? nb : T.n_end - 1;
-        st.a[j] = *(const uint4*)(T.a + ma * T.lda + k0 + kc * 16);
-        st.b[j] = *(const uint4*)(T.b + nb * T.ldb + k0 + kc * 16);
-    }
-    if (t < 128) {
-        int64_t m = T.m0 + t;
+    for (int ins = 0; ins < BM / 8 / WAVES; ins++) {
+        const int row0 = (ins * WAVES + wave) * 8;
+        const int row = row0 + (lane >> 3);
+        int64_t m = T.m0 + row;
         m = m < T.m_end ? m : T.m_end - 1;
-        st.s = T.sa[g * T.ldsa + m];
-    } else if (KIND == 1) {
-        int64_t n = T.n0 + (t - 128);
-        n = n < T.n_end ? n : T.n_end - 1;
-        st.s = T.sb[g * T.sb_s0 + n];
+        const uint8_t* src = T.a + m * T.lda + k0 + (((lane & 7) ^ swz(row)) << 4);
+        dma16(src, lds_addr(stage + Lds<ACC>::A + row0 * 128));
     }
-    if (KIND == 0) st.sbk = T.sb[(T.n0 >> 7) * T.sb_s0 + g * T.sb_s1];
-}
-
-template <int KIND>
-__device__ __forceinline__ void store_scales(const Stage& st, float* lsa, float* lsb, int t) {
-    if (t < 128)
-        lsa[t] = st.s;
-    else if (KIND == 1)
-        lsb[t - 128] = st.s;
+#pragma unroll
+    for (int ins = 0; ins < BN / 8 / WAVES; ins++) {
+        const int row0 = (ins * WAVES + wave) * 8;
+        const int row = row0 + (lane >> 3);
+        int64_t n = T.n0 + row;
+        n = n < T.n_end ? n : T.n_end - 1;
+        const uint8_t* src = T.b + n * T.ldb + k0 + (((lane & 7) ^ swz(row)) << 4);
+        dma16(src, lds_addr(stage + Lds<ACC>::B + row0 * 128));
+    }
+    // scales: the first waves load sa (64 floats per instruction); the
+    // waves after them load the B scales -- BN per-column floats (tile
+    // kind) or the BN/128 block scalars of this group (block kind)
+    constexpr int SA_INS = BM / 64, SB_INS = BN / 64;
+    if (wave < SA_INS) {
+        int64_t m = T.m0 + wave * 64 + lane;
+        m = m < T.m_end ? m : T.m_end - 1;
+        dma4(T.sa + g * T.ldsa + m, lds_addr(stage + Lds<ACC>::SA + wave * 256));
+    } else if (KIND == 1 && wave < SA_INS + SB_INS) {
+        const int w = wave - SA_INS;
+        int64_t n = T.n0 + w * 64 + lane;
+        n = n < T.n_end ? n : T.n_end - 1;
+        dma4(T.sb + g * T.sb_s0 + n, lds_addr(stage + Lds<ACC>::SB + w * 256));
+    } else if (KIND == 0 && wave == SA_INS && lane < BN / 128) {
+        int64_t blk = (T.n0 >> 7) + lane;
+        const int64_t last = (T.n_end - 1) >> 7;
+        blk = blk < last ? blk : last;
+        dma4(T.sb + blk * T.sb_s0 + g * T.sb_s1, lds_addr(stage + Lds<ACC>::SB));
+    }
 }
 
 // ==== ACC_F32 path: exact f16 widening, f16 matrix cores =============================
 //
-// LDS tile: 128 rows x 128 f16 = 256 B per row, 16 chunks of 16 B, chunk c
-// of row r stored at position c ^ (r & 15).
+// v_mfma_f32_32x32x16_f16: lane l feeds row l%32 of its operand with 8
+// values per k-step.  Lane l reads the 16-byte chunk c = 2q + l/32 of its
+// row (q = 0..3) and widens it to 16 f16: the first 8 feed k-step 2q, the
+// last 8 k-step 2q+1.
 
-constexpr int F16_TILE = 128 * 256;  // bytes
-
-__device__ __forceinline__ int f16_off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-
-// 16 E4M3 codes -> 16 f16 values (exact), as two 16-byte chunks.
-__device__ __forceinline__ void widen16(uint4 v, uint4& lo, uint4& hi) {
+__device__ __forceinline__ void f16_pair(const uint8_t* tile, int row, int chunk, v8h& lo, v8h& hi) {
+    const uint4 v = *(const uint4*)(tile + f8_off(row, chunk));
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t h[8];
+    v2h p[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
-        h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
     }
-    lo = make_uint4(h[0], h[1], h[2], h[3]);
-    hi = make_uint4(h[4], h[5], h[6], h[7]);
-}
-
-__device__ __forceinline__ void store_stage_f16(const Stage& st, uint8_t* la, uint8_t* lb, int t) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int cid = t + 256 * j;
-        const int row = cid >> 3, kc = cid & 7;
-        uint4 lo, hi;
-        widen16(st.a[j], lo, hi);
-        *(uint4*)(la + f16_off(row, 2 * kc)) = lo;
-        *(uint4*)(la + f16_off(row, 2 * kc + 1)) = hi;
-        widen16(st.b[j], lo, hi);
-        *(uint4*)(lb + f16_off(row, 2 * kc)) = lo;
-        *(uint4*)(lb + f16_off(row, 2 * kc + 1)) = hi;
+    for (int i = 0; i < 4; i++) {
+        lo[2 * i] = p[i][0];
+        lo[2 * i + 1] = p[i][1];
+        hi[2 * i] = p[4 + i][0];
+        hi[2 * i + 1] = p[4 + i][1];
     }
-}
-
-__device__ __forceinline__ v8h f16_frag(const uint8_t* tile, int row, int chunk) {
-    return __builtin_bit_cast(v8h, *(const uint4*)(tile + f16_off(row, chunk)));
 }
 
 // acc[i][j]: 32x32 sub-tile (m-sub i, n-sub j) of this wave, D^T layout:
 // register r of lane l is n = 32j + 8(r/4) + 4(l/32) + r%4, m = 32i + l%32.
 template <int KIND>
-__device__ __forceinline__ void mainloop_f32(const Tile& T, int64_t g0, int64_t g1, v16f (&acc)[2][2],
-                                             uint8_t* smem, float* ssa, float* ssb) {
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+__device__ __forceinline__ void compute_f32(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
+                                            int lane, int m_valid, v16f (&acc)[2][2]) {
+    const uint8_t* la = stage + Lds<0>::A;
+    const uint8_t* lb = stage + Lds<0>::B;
+    const float* lsa = (const float*)(stage + Lds<0>::SA);
+    const float* lsb = (const float*)(stage + Lds<0>::SB);
+    const int mbase = wm * 64, nbase = wn * 64;
+    if (mbase >= m_valid) return;  // this wave's rows are all past the end
+    const float sbk = KIND == 0 ? lsb[nbase >> 7] : 0.f;
+
+    v16f p[2][2];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-    if (g0 >= g1) return;
-
-    Stage st;
-    load_stage<KIND>(st, T, g0, t);
-    store_stage_f16(st, smem, smem + F16_TILE, t);
-    store_scales<KIND>(st, ssa, ssb, t);
-    float sbk = st.sbk;
-    __syncthreads();
-
-    for (int64_t g = g0; g < g1; g++) {
-        const int buf = (int)((g - g0) & 1);
-        const bool more = g + 1 < g1;
-        if (more) load_stage<KIND>(st, T, g + 1, t);
-
-        const uint8_t* la = smem + buf * 2 * F16_TILE;
-        const uint8_t* lb = la + F16_TILE;
-        const float* lsa = ssa + buf * 128;
-        const float* lsb = ssb + buf * 128;
-
-        v16f p[2][2];
+            for (int r = 0; r < 16; r++) p[i][j][r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int chunk = 2 * q + (lane >> 5);
+        v8h a0[2], a1[2], b0[2], b1[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) f16_pair(la, mbase + 32 * i + (lane & 31), chunk, a0[i], a1[i]);
+#pragma unroll
+        for (int j = 0; j < 2; j++) f16_pair(lb, nbase + 32 * j + (lane & 31), chunk, b0[j], b1[j]);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], p[i][j], 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < 16; r++) p[i][j][r] = 0.f;
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            const int chunk = 2 * s + (lane >> 5);
-            v8h af[2], bf[2];
+            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], p[i][j], 0, 0, 0);
+    }
 #pragma unroll
-            for (int i = 0; i < 2; i++) af[i] = f16_frag(la, wm * 64 + 32 * i + (lane & 31), chunk);
+    for (int i = 0; i < 2; i++) {
+        const float sam = lsa[mbase + 32 * i + (lane & 31)];
+        const float c = KIND == 0 ? sam * sbk : sam;
 #pragma unroll
-            for (int j = 0; j < 2; j++) bf[j] = f16_frag(lb, wn * 64 + 32 * j + (lane & 31), chunk);
+        for (int j = 0; j < 2; j++) {
+            if (KIND == 0) {
+                acc[i][j] += p[i][j] * c;
+            } else {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+                for (int q = 0; q < 4; q++) {
+                    const v4f sbn = *(const v4f*)(lsb + nbase + 32 * j + 8 * q + 4 * (lane >> 5));
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], p[i][j], 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const float sam = lsa[wm * 64 + 32 * i + (lane & 31)];
-            const float c = KIND == 0 ? sam * sbk : sam;
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                if (KIND == 0) {
-                    acc[i][j] += p[i][j] * c;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const v4f sbn = *(const v4f*)(lsb + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5));
-#pragma unroll
-                        for (int e = 0; e < 4; e++) acc[i][j][4 * q + e] += (p[i][j][4 * q + e] * c) * sbn[e];
-                    }
+                    for (int e = 0; e < 4; e++) acc[i][j][4 * q + e] += (p[i][j][4 * q + e] * c) * sbn[e];
                 }
             }
         }
-
-        if (more) {
-            const int nb = buf ^ 1;
-            uint8_t* na = smem + nb * 2 * F16_TILE;
-            store_stage_f16(st, na, na + F16_TILE, t);
-            store_scales<KIND>(st, ssa + nb * 128, ssb + nb * 128, t);
-            sbk = st.sbk;
-        }
-        __syncthreads();
     }
 }
+
+// ==== ACC_MFMA8 path: FP8 matrix cores, one MFMA per K group =============================
+//
+// Lane l feeds bytes [32(l/16), 32(l/16)+32) of its row: chunks 2(l/16) and
+// 2(l/16)+1.
+
+__device__ __forceinline__ v8i f8_frag(const uint8_t* tile, int row, int c0) {
+    const uint4 lo = *(const uint4*)(tile + f8_off(row, c0));
+    const uint4 hi = *(const uint4*)(tile + f8_off(row, c0 + 1));
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ v4f mfma8_group(const v8i& a, const v8i& b) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // formats 0/0: both operands FP8 E4M3; no in-instruction scaling
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// acc[i][j]: 16x16 sub-tile (m-sub i, n-sub j), D^T layout: register e of
+// lane l is n = 16j + 4(l/16) + e, m = 16i + l%16.
+template <int KIND>
+__device__ __forceinline__ void compute_mfma8(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
+                                              int lane, int m_valid, v4f (&acc)[4][4]) {
+    const uint8_t* la = stage + Lds<1>::A;
+    const uint8_t* lb = stage + Lds<1>::B;
+    const float* lsa = (const float*)(stage + Lds<1>::SA);
+    const float* lsb = (const float*)(stage + Lds<1>::SB);
+    const int mbase = wm * 64, nbase = wn * 64;
+    const int c0 = 2 * (lane >> 4);
+    if (mbase >= m_valid) return;
+    const float sbk = KIND == 0 ? lsb[nbase >> 7] : 0.f;
+
+    v8i bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) bf[j] = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+    v4f sbn[4];
+    if (KIND == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) sbn[j] = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (mbase + 16 * i >= m_valid) break;  // wave-uniform
+        const int mrow = mbase + 16 * i + (lane & 15);
+        const v8i af = f8_frag(la, mrow, c0);
+        const float sam = lsa[mrow];
+        const float c = KIND == 0 ? sam * sbk : sam;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const v4f p = mfma8_group(bf[j], af);
+            if (KIND == 0)
+                acc[i][j] += p * c;
+            else
+                acc[i][j] += (p * c) * sbn[j];
+        }
+    }
+}
+
+// ==== epilogue ===========================================================================
 
 // Store four consecutive columns n..n+3 of row m (masked at the edges).
 template <int OUT_F32>
@@ -281,177 +375,105 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
 }
 
 template <int OUT_F32>
-__device__ __forceinline__ void store_tile_f32(const v16f (&acc)[2][2], int64_t m0, int64_t m_end, int64_t n0,
-                                               int64_t n_end, void* d, int64_t ldd) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+__device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T, int wm, int wn, int lane,
+                                          void* d, int64_t ldd) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int64_t m = m0 + wm * 64 + 32 * i + (lane & 31);
-        if (m >= m_end) continue;
+        const int64_t m = T.m0 + wm * 64 + 32 * i + (lane & 31);
+        if (m >= T.m_end) continue;
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const int64_t n = n0 + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
-                if (n >= n_end) continue;
-                store4<OUT_F32>(d, ldd, m, n, n_end, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                const int64_t n = T.n0 + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
+                if (n >= T.n_end) continue;
+                store4<OUT_F32>(d, ldd, m, n, T.n_end, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                 acc[i][j][4 * q + 3]);
             }
     }
 }
 
-// ==== ACC_MFMA8 path: FP8 matrix cores, one MFMA per K group =============================
-//
-// LDS tile: 128 rows x 128 B, 8 chunks of 16 B, chunk c of row r stored at
-// position c ^ ((r ^ r>>3) & 7).
-
-constexpr int F8_TILE = 128 * 128;
-
-__device__ __forceinline__ int f8_off(int row, int chunk) {
-    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-__device__ __forceinline__ void store_stage_f8(const Stage& st, uint8_t* la, uint8_t* lb, int t) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int cid = t + 256 * j;
-        const int row = cid >> 3, kc = cid & 7;
-        *(uint4*)(la + f8_off(row, kc)) = st.a[j];
-        *(uint4*)(lb + f8_off(row, kc)) = st.b[j];
-    }
-}
-
-__device__ __forceinline__ v8i f8_frag(const uint8_t* tile, int row, int c0) {
-    const uint4 lo = *(const uint4*)(tile + f8_off(row, c0));
-    const uint4 hi = *(const uint4*)(tile + f8_off(row, c0 + 1));
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
-}
-
-__device__ __forceinline__ v4f mfma8_group(const v8i& a, const v8i& b) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    // formats 0/0: both operands FP8 E4M3; no in-instruction scaling
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-// acc[i][j]: 16x16 sub-tile (m-sub i, n-sub j), D^T layout: register e of
-// lane l is n = 16j + 4(l/16) + e, m = 16i + l%16.
-template <int KIND>
-__device__ __forceinline__ void mainloop_mfma8(const Tile& T, int64_t g0, int64_t g1, v4f (&acc)[4][4],
-                                               uint8_t* smem, float* ssa, float* ssb) {
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int c0 = 2 * (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (g0 >= g1) return;
-
-    Stage st;
-    load_stage<KIND>(st, T, g0, t);
-    store_stage_f8(st, smem, smem + F8_TILE, t);
-    store_scales<KIND>(st, ssa, ssb, t);
-    float sbk = st.sbk;
-    __syncthreads();
-
-    for (int64_t g = g0; g < g1; g++) {
-        const int buf = (int)((g - g0) & 1);
-        const bool more = g + 1 < g1;
-        if (more) load_stage<KIND>(st, T, g + 1, t);
-
-        const uint8_t* la = smem + buf * 2 * F8_TILE;
-        const uint8_t* lb = la + F8_TILE;
-        const float* lsa = ssa + buf * 128;
-        const float* lsb = ssb + buf * 128;
-
-        v8i bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) bf[j] = f8_frag(lb, wn * 64 + 16 * j + (lane & 15), c0);
-        v4f sbn[4];
-        if (KIND == 1) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) sbn[j] = *(const v4f*)(lsb + wn * 64 + 16 * j + 4 * (lane >> 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int mrow = wm * 64 + 16 * i + (lane & 15);
-            const v8i af = f8_frag(la, mrow, c0);
-            const float sam = lsa[mrow];
-            const float c = KIND == 0 ? sam * sbk : sam;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const v4f p = mfma8_group(bf[j], af);
-                if (KIND == 0)
-                    acc[i][j] += p * c;
-                else
-                    acc[i][j] += (p * c) * sbn[j];
-            }
-        }
-
-        if (more) {
-            const int nb = buf ^ 1;
-            uint8_t* na = smem + nb * 2 * F8_TILE;
-            store_stage_f8(st, na, na + F8_TILE, t);
-            store_scales<KIND>(st, ssa + nb * 128, ssb + nb * 128, t);
-            sbk = st.sbk;
-        }
-        __syncthreads();
-    }
-}
-
 template <int OUT_F32>
-__device__ __forceinline__ void store_tile_mfma8(const v4f (&acc)[4][4], int64_t m0, int64_t m_end, int64_t n0,
-                                                 int64_t n_end, void* d, int64_t ldd) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+__device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& T, int wm, int wn, int lane,
+                                            void* d, int64_t ldd) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int64_t m = m0 + wm * 64 + 16 * i + (lane & 15);
-        if (m >= m_end) continue;
+        const int64_t m = T.m0 + wm * 64 + 16 * i + (lane & 15);
+        if (m >= T.m_end) continue;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int64_t n = n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
-            if (n >= n_end) continue;
-            store4<OUT_F32>(d, ldd, m, n, n_end, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            const int64_t n = T.n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
+            if (n >= T.n_end) continue;
+            store4<OUT_F32>(d, ldd, m, n, T.n_end, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
     }
+}
+
+// ==== one tile: pipelined K loop, then the store ==============================================
+
+template <int ACC, int KIND, int OUT_F32>
+__device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, void* d, int64_t ldd,
+                                         uint8_t* smem) {
+    constexpr int S = Cfg<ACC>::STAGES;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave % Cfg<ACC>::WGM, wn = wave / Cfg<ACC>::WGM;
+    const int m_valid = (int)(T.m_end - T.m0 < Cfg<ACC>::BM ? T.m_end - T.m0 : Cfg<ACC>::BM);
+
+    typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;
+    AccT acc;
+    if constexpr (ACC == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // prologue: groups g0 .. g0+S-2
+#pragma unroll
+    for (int s = 0; s < S - 1; s++)
+        if (g0 + s < g1) issue_stage<ACC, KIND>(T, g0 + s, smem + s * Lds<ACC>::STAGE, wave, lane);
+
+    // Tile loads per group per wave; waves that also load scales issue one
+    // more, so waiting for PER outstanding is conservative for them.
+    constexpr int PER = (Cfg<ACC>::BM + Cfg<ACC>::BN) / 8 / WAVES;
+    static_assert(S == 2 || (S == 3 && PER == 6), "wait counts cover these pipelines");
+    for (int64_t g = g0; g < g1; g++) {
+        const int64_t it = g - g0;
+        // group g has landed (at most the following group still in flight)
+        // for every wave, and every wave is done with the stage of g-1
+        if (S == 3 && g + 1 < g1)
+            wait_and_barrier<6>();
+        else
+            wait_and_barrier<0>();
+        if (g + S - 1 < g1)
+            issue_stage<ACC, KIND>(T, g + S - 1, smem + ((it + S - 1) % S) * Lds<ACC>::STAGE, wave, lane);
+        const uint8_t* stage = smem + (it % S) * Lds<ACC>::STAGE;
+        if constexpr (ACC == 0)
+            compute_f32<KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+        else
+            compute_mfma8<KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+    }
+    wait_and_barrier<0>();  // the LDS stages may be reused by a following tile
+
+    if constexpr (ACC == 0)
+        store_f32<OUT_F32>(acc, T, wm, wn, lane, d, ldd);
+    else
+        store_mfma8<OUT_F32>(acc, T, wm, wn, lane, d, ldd);
 }
 
 // ==== kernels ==========================================================================
 
-// LDS: two stages of both tiles plus two stages of 128 scales for A and B.
-template <int ACC>
-struct Smem {
-    static constexpr int TILE = ACC == 0 ? F16_TILE : F8_TILE;
-    static constexpr int BYTES = 2 * 2 * TILE;
-};
-
-// One tile over K groups [g0, g1), then its store.
-template <int ACC, int KIND, int OUT_F32>
-__device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, void* d, int64_t ldd,
-                                         uint8_t* smem, float* ssa, float* ssb) {
-    if (ACC == 0) {
-        v16f acc[2][2];
-        mainloop_f32<KIND>(T, g0, g1, acc, smem, ssa, ssb);
-        store_tile_f32<OUT_F32>(acc, T.m0, T.m_end, T.n0, T.n_end, d, ldd);
-    } else {
-        v4f acc[4][4];
-        mainloop_mfma8<KIND>(T, g0, g1, acc, smem, ssa, ssb);
-        store_tile_mfma8<OUT_F32>(acc, T.m0, T.m_end, T.n0, T.n_end, d, ldd);
-    }
-}
-
 template <int ACC, int KIND, int OUT_F32, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<ACC>::BYTES];
-    __shared__ __attribute__((aligned(16))) float ssa[2 * 128];
-    __shared__ __attribute__((aligned(16))) float ssb[2 * 128];
-
+__global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<ACC>::BYTES];
     const int64_t ntiles = tiles_m * tiles_n;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t split = SPLIT ? wid / ntiles : 0;
@@ -459,9 +481,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int64_t tiles_m, 
     tile_coords(wid % ntiles, tiles_m, tiles_n, tm, tn);
 
     Tile T;
-    T.m0 = tm * BM;
+    T.m0 = tm * Cfg<ACC>::BM;
     T.m_end = p.M;
-    T.n0 = tn * BN;
+    T.n0 = tn * Cfg<ACC>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -474,24 +496,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int64_t tiles_m, 
     T.sb_s1 = p.sb_s1;
 
     const int64_t groups = p.K / 128;
-    int64_t g0 = 0, g1 = groups;
     if (SPLIT) {
         const int64_t per = (groups + p.splits - 1) / p.splits;
-        g0 = split * per;
-        g1 = g0 + per < groups ? g0 + per : groups;
-        run_tile<ACC, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem, ssa, ssb);
+        const int64_t g0 = split * per;
+        const int64_t g1 = g0 + per < groups ? g0 + per : groups;
+        run_tile<ACC, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
     } else {
-        run_tile<ACC, KIND, OUT_F32>(T, g0, g1, p.d, p.ldd, smem, ssa, ssb);
+        run_tile<ACC, KIND, OUT_F32>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
 
 // Grouped: workgroup (expert e, n-tile) walks the expert's m-tiles.
 template <int ACC, int OUT_F32>
-__global__ __launch_bounds__(256) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<ACC>::BYTES];
-    __shared__ __attribute__((aligned(16))) float ssa[2 * 128];
-    __shared__ __attribute__((aligned(16))) float ssb[2 * 128];
-
+__global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<ACC>::BYTES];
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t e = wid / tiles_n;
     const int64_t tn = wid % tiles_n;
@@ -499,7 +517,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(GemmArgs p, int64_t tiles_
 
     Tile T;
     T.m_end = r1;
-    T.n0 = tn * BN;
+    T.n0 = tn * Cfg<ACC>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -510,9 +528,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(GemmArgs p, int64_t tiles_
     T.sb = p.sb + e * p.sb_estride;
     T.sb_s0 = p.K / 128;
     T.sb_s1 = 1;
-    for (int64_t m0 = r0; m0 < r1; m0 += BM) {
+    for (int64_t m0 = r0; m0 < r1; m0 += Cfg<ACC>::BM) {
         T.m0 = m0;
-        run_tile<ACC, 0, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem, ssa, ssb);
+        run_tile<ACC, 0, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
     }
 }
 
@@ -538,11 +556,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ==== host side ==========================================================================
 
+// The split count is chosen from the f16-path tile (the smaller one) so the
+// workspace query does not depend on the accumulation mode.
 int gemm_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t tiles = ((M + Cfg<0>::BM - 1) / Cfg<0>::BM) * ((N + Cfg<0>::BN - 1) / Cfg<0>::BN);
     const int64_t groups = K / 128;
-    if (tiles == 0 || groups < 16 || tiles >= 256) return 1;
-    int64_t s = 512 / tiles;         // aim for ~2 workgroups per CU
+    if (tiles == 0 || groups < 16 || tiles >= 128) return 1;
+    int64_t s = 256 / tiles;         // about one workgroup per CU
     const int64_t cap = groups / 8;  // at least 8 groups per split
     if (s > cap) s = cap;
     if (s > 256) s = 256;
@@ -557,13 +577,14 @@ size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
 
 template <int ACC, int KIND, int OUT_F32, bool SPLIT>
 static void launch_dense(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, int64_t wgs, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<ACC, KIND, OUT_F32, SPLIT>), dim3((unsigned)wgs), dim3(256), 0, st, g,
+    hipLaunchKernelGGL((gemm_kernel<ACC, KIND, OUT_F32, SPLIT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g,
                        tiles_m, tiles_n);
 }
 
 template <int ACC>
 static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
-    const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int64_t tiles_m = (g.M + Cfg<ACC>::BM - 1) / Cfg<ACC>::BM;
+    const int64_t tiles_n = (g.N + Cfg<ACC>::BN - 1) / Cfg<ACC>::BN;
     if (g.splits > 1) {
         const int64_t wgs = tiles_m * tiles_n * g.splits;
         if (g.bscale_kind == 0)
@@ -604,12 +625,12 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 template <int ACC>
 static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
-    const int64_t tiles_n = g.N / BN;
+    const int64_t tiles_n = (g.N + Cfg<ACC>::BN - 1) / Cfg<ACC>::BN;
     const dim3 grid((unsigned)(tiles_n * g.G));
     if (g.out_f32)
-        hipLaunchKernelGGL((grouped_kernel<ACC, 1>), grid, dim3(256), 0, st, g, tiles_n);
+        hipLaunchKernelGGL((grouped_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
     else
-        hipLaunchKernelGGL((grouped_kernel<ACC, 0>), grid, dim3(256), 0, st, g, tiles_n);
+        hipLaunchKernelGGL((grouped_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
     return hipGetLastError();
 }
 
