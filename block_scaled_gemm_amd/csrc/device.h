@@ -23,26 +23,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // ---- E4M3 rounding -------------------------------------------------------------
 //
 // Code of the E4M3 value nearest to y, ties to the even code, |y| >= 448
-// saturating to 448, sign copied.  Integer form of round-to-nearest-even on
-// the fp32 bits: in the normal range, rounding the 23-bit mantissa to 3 bits
-// and re-biasing the exponent (127 -> 7) is (rounded_bits >> 20) - (120 << 3);
-// below 2^-6 the E4M3 step is 2^-9, so the code is rint(|y| * 512), where
-// rint (v_rndne_f32) rounds half to even and the multiply is exact.
+// saturating to 448, sign copied (so values rounding to zero keep it).
+// v_cvt_pk_fp8_f32 rounds to nearest even into OCP E4M3; clamping to
+// [-448, 448] first (v_med3_f32) gives the saturation.  Checked against the
+// CPU oracle's encoder over every finite fp32 bit pattern.
+__device__ __forceinline__ float sat448(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
+
 __device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
-    const uint32_t normal = (rounded >> 20) - (120u << 3);
-    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    uint32_t code = a < 0x3C800000u ? sub : normal;   // 2^-6
-    code = a >= 0x43E00000u ? 0x7Eu : code;            // 448
-    return code | sign;
+    const float c = sat448(y);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
 // Four codes packed little-endian into a dword.
 __device__ __forceinline__ uint32_t pack4(float y0, float y1, float y2, float y3) {
-    return e4m3_code(y0) | (e4m3_code(y1) << 8) | (e4m3_code(y2) << 16) | (e4m3_code(y3) << 24);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(y0), sat448(y1), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(y2), sat448(y3), lo, true);
 }
 
 // Quantise the 8 bf16 values of a uint4 (two per dword) with factor inv;
