@@ -1,6 +1,7 @@
 """Benchmark of the fine-grained FP8 linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum fp32|mfma8]
+    python bench.py --traffic-probe     # plain copy of known size, for counter scaling
 
 Workload: the dense Fprop at real width -- X[4096 x 7168] bf16 ~N(0,1) with
 0.1% x100 outliers, W[18432 x 7168] bf16 ~N(0,0.02).  One step is the whole
@@ -8,6 +9,9 @@ hot path over that batch, inputs already in HBM:
     quantise X in 1x128 tiles  (fp8_quant_tile, FP32 scales)
     quantise W in 128x128 blocks (fp8_quant_block, FP32 scales)
     Y = X W^T, block-scaled FP8 GEMM with per-128 FP32 promotion, bf16 out.
+The GEMM's accumulation mode is --accum (fp32: exact group partials on the
+f16 matrix cores; mfma8: group partials from the FP8 matrix cores); the
+other mode's GEMM is timed as well and reported under `gemm_modes`.
 
 Prints one JSON line.  `value` is the step's GEMM FLOPs over the step time
 (quantisation included); `roofline` covers the dominant kernel (the GEMM),
@@ -30,7 +34,7 @@ sys.path.insert(0, ROOT)
 M, N, K = 4096, 18432, 7168
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_fprop_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_fprop_traffic.txt")
 KERNEL_SOURCES = ["block_scaled_gemm_amd/csrc/gemm.hip", "block_scaled_gemm_amd/csrc/device.h"]
 
 
@@ -52,17 +56,37 @@ def quant_bytes_block(rows, cols):
     return rows * cols * 3 + ((rows + 127) // 128) * (cols // 128) * 4
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs,
-    or None when absent or taken on a different kernel source."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source.
+    The summary is text: `key: value` lines."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
         return None
-    if t.get("source_hash") != source_hash(KERNEL_SOURCES):
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_hash") != source_hash(KERNEL_SOURCES) or kv.get("kernel") != kernel:
         return None
-    return t.get("bytes_per_launch")
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe():
+    """A plain copy of known size (y = -x over 2^28 fp32: 1 GiB read, 1 GiB
+    written), launched 3 times, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "torch.neg fp32", "elements": n, "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(X, W, target_s=20.0):
@@ -99,15 +123,26 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--accum", choices=["fp32", "mfma8"], default="fp32",
+                    help="GEMM accumulation: exact group partials (fp32) or FP8 matrix cores (mfma8)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only a plain copy of known size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "
               "single-GPU build (no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_probe:
+        traffic_probe()
+        return
+
     import torch
     import block_scaled_gemm_amd as bs
     from block_scaled_gemm_amd import inputs
+    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8}[args.accum]
+    other = "mfma8" if args.accum == "fp32" else "fp32"
+    kernel = f"gemm_kernel<{accum}, 0, 0, false>"
 
     t_gen = time.perf_counter()
     d = inputs.dense_fprop()
@@ -132,7 +167,8 @@ def main():
         bs.fp8_quant_block(W, bs.SCALE_FP32, q=qw, s=sw)
         if ev is not None:
             ev[2].record()
-        bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y)
+        bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y,
+                                accum=accum)
         if ev is not None:
             ev[3].record()
 
@@ -155,10 +191,24 @@ def main():
     print(f"[bench] {args.steps} steps: {step_ms:.3f} ms/step (quant X {qx_ms:.3f}, quant W {qw_ms:.3f}, "
           f"gemm {gemm_ms:.3f} ms)", file=sys.stderr, flush=True)
 
+    # the same GEMM in the other accumulation mode, outside the timed steps
+    other_accum = bs.ACCUM_MFMA8 if accum == bs.ACCUM_FP32 else bs.ACCUM_FP32
+    oe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y,
+                            accum=other_accum)
+    for e in oe:
+        e[0].record()
+        bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y,
+                                accum=other_accum)
+        e[1].record()
+    torch.cuda.synchronize()
+    other_ms = np.mean([e[0].elapsed_time(e[1]) for e in oe])
+
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     bx, bw = quant_bytes_row(M, K), quant_bytes_block(N, K)
-    traffic = measured_traffic()
+    traffic = measured_traffic(kernel)
+    flops_tf = lambda ms: flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (% MFMA peak); quantize GB/s (% HBM peak)",
         "value": flops / (step_ms * 1e-3) / 1e12,
@@ -170,15 +220,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "dtype": "fp8_e4m3",
         "data": "synthetic (seeded numpy: N(0,1) with 0.1% x100 outliers; N(0,0.02))",
         "config": {"workload": "dense Fprop: quant X[4096x7168] 1x128 + quant W[18432x7168] 128x128 "
                                "+ GEMM 4096x18432x7168 -> bf16",
-                   "M": M, "N": N, "K": K, "scales": "fp32"},
+                   "M": M, "N": N, "K": K, "scales": "fp32", "accum": args.accum},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_FP8_TFLOPS,
-                     "traffic": traffic, "kernel": "gemm_kernel<0,0,false>",
-                     "kernel_ms": gemm_ms},
+                     "traffic": traffic, "kernel": kernel, "kernel_ms": gemm_ms},
+        "gemm_modes": {
+            args.accum: {"ms": gemm_ms, "TFLOP/s": flops_tf(gemm_ms),
+                         "frac_fp8_peak": flops_tf(gemm_ms) / PEAK_FP8_TFLOPS},
+            other: {"ms": other_ms, "TFLOP/s": flops_tf(other_ms),
+                    "frac_fp8_peak": flops_tf(other_ms) / PEAK_FP8_TFLOPS},
+        },
         "quantizers": {
             "quant_tile_row_X": {"ms": qx_ms, "GB/s": bx / (qx_ms * 1e-3) / 1e9,
                                  "frac_hbm": bx / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
