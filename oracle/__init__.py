@@ -56,6 +56,9 @@ def _declare(L):
     L.orc_quant_block.restype = ctypes.c_int
     L.orc_quant_block.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int,
                                   _u8p, _i64, _u8p, _i64, _f32p, _i64]
+    L.orc_requant_col.restype = ctypes.c_int
+    L.orc_requant_col.argtypes = [_u8p, _i64, _i64, _i64, _f32p, _i64,
+                                  ctypes.c_int, _u8p, _i64, _f32p, _i64]
     L.orc_gemm.restype = ctypes.c_int
     L.orc_gemm.argtypes = [_i64, _i64, _i64, _u8p, _i64, _f32p, _i64,
                            _u8p, _i64, _f32p, ctypes.c_int, _i64, _i64,
@@ -78,12 +81,12 @@ def _declare(L):
 
 class Oracle:
     """The oracle library at `path` (default: oracle/liboracle.so, built on
-    first use when missing)."""
+    first use when missing or older than oracle.c)."""
 
     def __init__(self, path=None):
         if path is None:
             path = _build.LIB
-            if not os.path.exists(path):
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
                 _build.build()
         self.path = path
         self.L = _declare(ctypes.CDLL(path))
@@ -151,6 +154,21 @@ class Oracle:
                                       rows, _p(s, _f32p), s.shape[1]),
                "quant_block")
         return q, s, qt
+
+    def requant_col(self, q, s, pow2):
+        """Backward re-tiling: codes q[rows, cols] in 1x128 row groups with
+        scales s[cols/128, rows] -> (qt[cols, rows], st[rows/128, cols]) in
+        128x1 groups, as quant_tile's axis 1 lays them out."""
+        q = _c(q, np.uint8)
+        s = _c(s, np.float32)
+        rows, cols = q.shape
+        qt = np.empty((cols, rows), np.uint8)
+        st = np.empty((rows // 128, cols), np.float32)
+        _check(self.L.orc_requant_col(_p(q, _u8p), rows, cols, cols,
+                                      _p(s, _f32p), s.shape[1], int(pow2),
+                                      _p(qt, _u8p), rows, _p(st, _f32p), cols),
+               "requant_col")
+        return qt, st
 
     # ---- GEMM --------------------------------------------------------------
 
@@ -263,6 +281,10 @@ def quant_tile(x, axis, pow2):
 
 def quant_block(w, pow2, transpose=False):
     return default().quant_block(w, pow2, transpose)
+
+
+def requant_col(q, s, pow2):
+    return default().requant_col(q, s, pow2)
 
 
 def gemm(a, sa, b, sb, bscale_kind, sb_s0, sb_s1):

@@ -266,6 +266,50 @@ int orc_quant_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ldw,
 }
 
 /* ------------------------------------------------------------------------
+ * Backward re-tiling ([hacks-368261], the hardware-suggestions passage on
+ * the backward pass): a matrix held as FP8 codes in 1x128 row groups is read
+ * back, dequantised, transposed and quantised again in 128x1 groups.
+ * Readings (the pages give the four steps only): the dequantised element is
+ * the fp32 product fl32(dec(q) * s), fp32 being the precision of the stored
+ * scale; the new groups take their amax over those fp32 values and follow
+ * the same scale rule, amax floor and rounding as the quantisers above.
+ * ------------------------------------------------------------------------ */
+int orc_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                    const float *s, int64_t lds, int pow2, uint8_t *qt,
+                    int64_t ldqt, float *st, int64_t ldst)
+{
+    if (!q || !s || !qt || !st || rows < 0 || cols < 0)
+        return ORC_ERR_ARG;
+    if (rows % 128 != 0 || cols % 128 != 0)
+        return ORC_ERR_SHAPE;
+    if (ldq < cols || lds < rows || ldqt < rows || ldst < cols)
+        return ORC_ERR_ARG;
+    int64_t c;
+#pragma omp parallel for schedule(static)
+    for (c = 0; c < cols; c++) {
+        float x[128];
+        for (int64_t g = 0; g < rows / 128; g++) {
+            /* read back and dequantise the column's 128 elements of group g */
+            float amax = 0.0f;
+            for (int64_t i = 0; i < 128; i++) {
+                int64_t r = g * 128 + i;
+                float d = (float)orc_e4m3_decode(q[r * ldq + c]); /* exact */
+                x[i] = d * s[(c / 128) * lds + r];                /* fp32 */
+                if (fabsf(x[i]) > amax)
+                    amax = fabsf(x[i]);
+            }
+            /* quantise again as a 128x1 group, written transposed */
+            float sc, inv;
+            orc_group_scale(amax, pow2, &sc, &inv);
+            st[g * ldst + c] = sc;
+            for (int64_t i = 0; i < 128; i++)
+                qt[c * ldqt + g * 128 + i] = orc_e4m3_encode(x[i] * inv);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
  * GEMM reference.  Every finite E4M3 value is an integer multiple of 2^-9
  * with magnitude at most 448 = 229376 * 2^-9, so dec(a) * dec(b) is an
  * integer multiple of 2^-18 below 2^36 in units, and a 128-term group sum is

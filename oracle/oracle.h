@@ -74,6 +74,17 @@ int orc_quant_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ldw,
                     int pow2, uint8_t *q, int64_t ldq, uint8_t *qt,
                     int64_t ldqt, float *s, int64_t lds);
 
+/* ---- backward re-tiling ----------------------------------------------------
+ * q [rows][ldq] holds codes quantised in 1x128 row groups with scales
+ * s[g*lds + r] (the layout orc_quant_tile writes for axis 0).  The matrix is
+ * dequantised (x = fl32(dec(q) * s)), transposed and quantised again in
+ * 128x1 groups down its columns: qt [cols][ldqt], scale of group g of column
+ * c in st[g*ldst + c] (the layout of axis 1).  rows and cols must be
+ * multiples of 128. */
+int orc_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                    const float *s, int64_t lds, int pow2, uint8_t *qt,
+                    int64_t ldqt, float *st, int64_t ldst);
+
 /* ---- block-scaled GEMM ---------------------------------------------------
  * R[m][n] = sum_g sa[g*ldsa+m] * SB(n,g) * P_g[m][n], with
  *   P_g[m][n] = sum_{k in group g} dec(a[m*lda+k]) * dec(b[n*ldb+k])

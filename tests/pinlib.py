@@ -182,10 +182,17 @@ def check_worked_examples(orc):
 
 
 def brute_group(bits, pow2, table):
-    """Independent brute force for one group: amax from the float values, the
-    scale by trying every power of two (POW2) or by the fp32 quotient, and
-    every code by scanning all 254 finite codes for the nearest value."""
-    x = bf16_f32(bits)
+    """Independent brute force for one group of bf16 bits (see
+    brute_group_f32)."""
+    return brute_group_f32(bf16_f32(bits), pow2, table)
+
+
+def brute_group_f32(x, pow2, table):
+    """Independent brute force for one group of fp32 values: amax from the
+    values, the scale by trying every power of two (POW2) or by the fp32
+    quotient, and every code by scanning all 254 finite codes for the
+    nearest value."""
+    x = np.asarray(x, np.float32)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
     floor_a = np.float32(448.0 * 2.0 ** -126)
     a = max(amax, floor_a)
@@ -333,6 +340,73 @@ def check_block_vs_rows(orc, seed=29):
         assert np.all(sr == sb[0][:, None])
 
 
+# ---- backward re-tiling ------------------------------------------------------------
+
+def check_requant_bruteforce(orc, seed=47):
+    """Re-tiling 1x128 codes into 128x1 groups: sampled output groups match
+    the brute-force group quantiser applied to the fp32 dequantised column
+    (numpy's IEEE fp32 product of the decoded code and its row scale)."""
+    rng = np.random.default_rng(seed)
+    table = orc.decode_table()
+    f = (rng.standard_normal((256, 256)) * 10.0 ** rng.uniform(-3, 3, (256, 1))).astype(np.float32)
+    f[rng.random(f.shape) < 0.01] *= 100
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    for pow2_in in (0, 1):
+        q, s = orc.quant_tile(bits, 0, pow2_in)
+        for pow2 in (0, 1):
+            qt, st = orc.requant_col(q, s, pow2)
+            assert qt.shape == (256, 256) and st.shape == (2, 256)
+            for c in (0, 77, 128, 255):
+                for g in (0, 1):
+                    rows = np.arange(g * 128, g * 128 + 128)
+                    xhat = table[q[rows, c]].astype(np.float32) * s[c // 128, rows]
+                    want, ws = brute_group_f32(xhat, pow2, table)
+                    np.testing.assert_array_equal(qt[c, g * 128:(g + 1) * 128], want,
+                                                  err_msg=f"in={pow2_in} out={pow2} col {c} group {g}")
+                    assert st[g, c] == ws
+
+
+def check_requant_exact_dequant(orc, seed=53):
+    """With power-of-two row scales the dequantised values (4 significant
+    bits) are exact bf16 numbers, so re-tiling must equal quantising that
+    exact matrix directly in 128x1 groups."""
+    rng = np.random.default_rng(seed)
+    table = orc.decode_table()
+    f = (rng.standard_normal((384, 256)) * 10.0 ** rng.uniform(-2, 2, (384, 1))).astype(np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    q, s = orc.quant_tile(bits, 0, 1)
+    xhat = table[q] * np.repeat(s.T, 128, axis=1).astype(np.float64)
+    xbits = f32_bf16_exact(xhat.astype(np.float32))
+    for pow2 in (0, 1):
+        qt, st = orc.requant_col(q, s, pow2)
+        qd, sd = orc.quant_tile(xbits, 1, pow2)
+        np.testing.assert_array_equal(qt, qd)
+        np.testing.assert_array_equal(st, sd)
+
+
+def check_requant_fp32_dequant(orc):
+    """Worked case for the reading that the dequantised element is the fp32
+    product fl32(dec(q) * s).  Column 0 holds 448 (code 0x7E, row scale 1)
+    and 1.25 (code 0x3A) with the row scale fl32(0.85) = 0.85000002384...:
+    the exact product 1.0625000298... lies just above 1.0625, the midpoint of
+    E4M3 1.0 (0x38) and 1.125 (0x39), but rounds to 1.0625 in fp32.  The
+    group amax is 448, so the new scale is 1 and the element's code is the
+    tie, broken to the even code 0x38 (rounding the exact product would give
+    0x39)."""
+    s1 = np.float32(0.85)
+    assert fractions.Fraction(5, 4) * fractions.Fraction(float(s1)) > fractions.Fraction(17, 16)
+    assert np.float32(1.25) * s1 == np.float32(1.0625)
+    q = np.zeros((128, 128), np.uint8)
+    s = np.ones((1, 128), np.float32)
+    q[0, 0], q[1, 0] = 0x7E, 0x3A
+    s[0, 1] = s1
+    for pow2 in (0, 1):
+        qt, st = orc.requant_col(q, s, pow2)
+        assert st[0, 0] == np.float32(1.0)
+        assert qt[0, 0] == 0x7E and qt[0, 1] == 0x38, (pow2, hex(qt[0, 1]))
+        assert np.all(qt[0, 2:] == 0)
+
+
 # ---- GEMM -------------------------------------------------------------------------
 
 def _random_codes(rng, shape, table):
@@ -459,4 +533,5 @@ ALL_CHECKS = [
     check_error_bound, check_transpose_symmetry, check_orientation,
     check_block_vs_rows, check_gemm_bruteforce, check_gemm_identity,
     check_gemm_integers, check_gemm_entries_and_grouped, check_scale_edges,
+    check_requant_bruteforce, check_requant_exact_dequant, check_requant_fp32_dequant,
 ]

@@ -59,6 +59,19 @@ MUTATIONS = {
     "tile_scale_per_block": (
         "return (double)sb[g * s0 + n];",
         "return (double)sb[g * s0 + (n / 128) * 128];"),
+    "requant_dequant_to_bf16": (
+        "x[i] = d * s[(c / 128) * lds + r];                /* fp32 */",
+        "{ float t = d * s[(c / 128) * lds + r]; uint32_t u; memcpy(&u, &t, 4);\n"
+        "  u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u; memcpy(&x[i], &u, 4); }"),
+    "requant_scale_wrong_row": (
+        "x[i] = d * s[(c / 128) * lds + r];",
+        "x[i] = d * s[(c / 128) * lds + (r ^ 1)];"),
+    "requant_amax_of_codes": (
+        "                if (fabsf(x[i]) > amax)\n                    amax = fabsf(x[i]);\n            }\n            /* quantise again",
+        "                if (fabsf(d) > amax)\n                    amax = fabsf(d);\n            }\n            /* quantise again"),
+    "requant_not_transposed": (
+        "qt[c * ldqt + g * 128 + i] = orc_e4m3_encode(x[i] * inv);",
+        "qt[(g * 128 + i) * cols + c] = orc_e4m3_encode(x[i] * inv);"),
     "b_reversed_within_group": (
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[k]];",
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[g * 128 + 127 - (k - g * 128)]];"),
