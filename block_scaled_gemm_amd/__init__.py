@@ -10,6 +10,8 @@ Functions carry the C names (see include/fp8bs.h for the full contract):
     fp8_cast_e4m3(x)                                -> q
     fp8_quant_tile(x, axis, scale_mode)             -> (q, s)
     fp8_quant_block(w, scale_mode, transpose=False) -> (q, s, qt)
+    fp8_quant_dual(x, scale_mode)                   -> (qr, sr, qc, sc)
+    fp8_requant_col(q, s, scale_mode)               -> (qt, st)
     fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype) -> d
     fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype, rows_bound=None)    -> d
 
@@ -59,6 +61,10 @@ def lib():
         L.fp8_quant_tile.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp]
         L.fp8_quant_block.restype = i32
         L.fp8_quant_block.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
+        L.fp8_quant_dual.restype = i32
+        L.fp8_quant_dual.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+        L.fp8_requant_col.restype = i32
+        L.fp8_requant_col.argtypes = [vp, i64, i64, i64, vp, i64, i32, vp, i64, vp, i64, vp]
         L.fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_blockscaled.restype = i32
@@ -152,6 +158,36 @@ def fp8_quant_block(w, scale_mode=SCALE_FP32, transpose=False, q=None, s=None, q
                                  _ptr(qt) if transpose else None, _ld(qt) if transpose else 0,
                                  _ptr(s), _ld(s), _stream()), "fp8_quant_block")
     return q, s, qt
+
+
+def fp8_quant_dual(x, scale_mode=SCALE_FP32):
+    """Both groupings of bf16 x [rows, cols] from one read: returns
+    (qr, sr, qc, sc) equal to fp8_quant_tile(x, ROW) and fp8_quant_tile(x, COL)."""
+    _dev(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    qr = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sr = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+    qc = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((rows // 128, cols), dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quant_dual(_ptr(x), rows, cols, _ld(x), int(scale_mode), _ptr(qr), _ld(qr), _ptr(sr),
+                                _ld(sr), _ptr(qc), _ld(qc), _ptr(sc), _ld(sc), _stream()), "fp8_quant_dual")
+    return qr, sr, qc, sc
+
+
+def fp8_requant_col(q, s, scale_mode=SCALE_FP32, qt=None, st=None):
+    """Backward re-tiling: codes q [rows, cols] in 1x128 row groups with
+    scales s [cols/128, rows] (fp8_quant_tile's ROW output) -> qt [cols, rows]
+    and st [rows/128, cols] in 128x1 groups (its COL layout)."""
+    _dev(q, "q", torch.uint8)
+    _dev(s, "s", torch.float32)
+    rows, cols = q.shape
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=q.device)
+    if st is None:
+        st = torch.empty((rows // 128, cols), dtype=torch.float32, device=q.device)
+    _check(lib().fp8_requant_col(_ptr(q), rows, cols, _ld(q), _ptr(s), _ld(s), int(scale_mode),
+                                 _ptr(qt), _ld(qt), _ptr(st), _ld(st), _stream()), "fp8_requant_col")
+    return qt, st
 
 
 # ---- GEMM -----------------------------------------------------------------------

@@ -105,6 +105,40 @@ FP8BS_EXPORT int fp8_quant_block(const uint16_t* w, int64_t rows, int64_t cols, 
                                                 ldqt, s, lds, (hipStream_t)stream));
 }
 
+FP8BS_EXPORT int fp8_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int scale_mode,
+                                uint8_t* qr, int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc,
+                                float* sc, int64_t ldsc, void* stream) {
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (rows < 0 || cols < 0) return FP8BS_ERR_ARG;
+    if (rows > 0 && cols > 0 && (!x || !qr || !sr || !qc || !sc)) return FP8BS_ERR_ARG;
+    if (rows % 128 != 0 || cols % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (ldx < cols || ldqr < cols || ldqc < rows || ldsr < rows || ldsc < cols) return FP8BS_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(qr, 16) || !aligned(qc, 16) || !aligned(sr, 4) || !aligned(sc, 4) ||
+        ldx % 8 != 0 || ldqr % 16 != 0 || ldqc % 16 != 0)
+        return FP8BS_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_quant_dual(x, rows, cols, ldx, scale_mode == FP8BS_SCALE_POW2, qr, ldqr, sr,
+                                               ldsr, qc, ldqc, sc, ldsc, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_requant_col(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                                 int64_t lds, int scale_mode, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                                 void* stream) {
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (rows < 0 || cols < 0) return FP8BS_ERR_ARG;
+    if (rows > 0 && cols > 0 && (!q || !s || !qt || !st)) return FP8BS_ERR_ARG;
+    if (rows % 128 != 0 || cols % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (ldq < cols || lds < rows || ldqt < rows || ldst < cols) return FP8BS_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 16) || !aligned(st, 4) || ldq % 16 != 0 ||
+        ldqt % 16 != 0 || lds % 4 != 0)
+        return FP8BS_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_requant_col(q, rows, cols, ldq, s, lds, scale_mode == FP8BS_SCALE_POW2, qt,
+                                                ldqt, st, ldst, (hipStream_t)stream));
+}
+
 FP8BS_EXPORT size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
     return fp8bs::gemm_workspace(M, N, K);

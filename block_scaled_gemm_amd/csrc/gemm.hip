@@ -56,32 +56,30 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr int THREADS = 512;
 constexpr int WAVES = THREADS / 64;
 
-template <int ACC>
-struct Cfg;
+// Workgroup tile shapes: 8 waves of 64 x 64 each, three K groups in flight.
+// Shape 0, 256 (m) x 128 (n), serves every launch.  (A 128 x 256 shape for
+// experts of about 128 rows measured no faster on the grouped workloads:
+// the 256-row tile reads each weight tile once per expert.)
+template <int SH>
+struct Shape;
 template <>
-struct Cfg<0> {  // f16 matrix cores
+struct Shape<0> {
     static constexpr int BM = 256, BN = 128;
-    static constexpr int WGM = 4, WGN = 2;  // wave grid (m, n): waves of 64 x 64
-    static constexpr int STAGES = 3;
-};
-template <>
-struct Cfg<1> {  // FP8 matrix cores
-    static constexpr int BM = 256, BN = 128;
-    static constexpr int WGM = 4, WGN = 2;  // waves of 64 x 64
+    static constexpr int WGM = 4, WGN = 2;  // wave grid (m, n)
     static constexpr int STAGES = 3;
 };
 
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
-template <int ACC>
+template <int SH>
 struct Lds {
-    static constexpr int BM = Cfg<ACC>::BM, BN = Cfg<ACC>::BN;
+    static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     static constexpr int A = 0;
     static constexpr int B = BM * 128;
     static constexpr int SA = B + BN * 128;
     static constexpr int SB = SA + BM * 4;
     static constexpr int STAGE = SB + BN * 4;
-    static constexpr int BYTES = STAGE * Cfg<ACC>::STAGES;
+    static constexpr int BYTES = STAGE * Shape<SH>::STAGES;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -161,9 +159,9 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
 
 // ---- staging: issue one K group of both tiles and their scales into a stage ---------------
 
-template <int ACC, int KIND>
+template <int SH, int KIND>
 __device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* stage, int wave, int lane) {
-    constexpr int BM = Cfg<ACC>::BM, BN = Cfg<ACC>::BN;
+    constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     const int64_t k0 = g * 128;
     // A: BM/8 instructions of 8 rows, spread over the waves
 #pragma unroll
@@ -173,7 +171,7 @@ __device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* s
         int64_t m = T.m0 + row;
         m = m < T.m_end ? m : T.m_end - 1;
         const uint8_t* src = T.a + m * T.lda + k0 + (((lane & 7) ^ swz(row)) << 4);
-        dma16(src, lds_addr(stage + Lds<ACC>::A + row0 * 128));
+        dma16(src, lds_addr(stage + Lds<SH>::A + row0 * 128));
     }
 #pragma unroll
     for (int ins = 0; ins < BN / 8 / WAVES; ins++) {
@@ -182,7 +180,7 @@ __device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* s
         int64_t n = T.n0 + row;
         n = n < T.n_end ? n : T.n_end - 1;
         const uint8_t* src = T.b + n * T.ldb + k0 + (((lane & 7) ^ swz(row)) << 4);
-        dma16(src, lds_addr(stage + Lds<ACC>::B + row0 * 128));
+        dma16(src, lds_addr(stage + Lds<SH>::B + row0 * 128));
     }
     // scales: the first waves load sa (64 floats per instruction); the
     // waves after them load the B scales -- BN per-column floats (tile
@@ -191,17 +189,17 @@ __device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* s
     if (wave < SA_INS) {
         int64_t m = T.m0 + wave * 64 + lane;
         m = m < T.m_end ? m : T.m_end - 1;
-        dma4(T.sa + g * T.ldsa + m, lds_addr(stage + Lds<ACC>::SA + wave * 256));
+        dma4(T.sa + g * T.ldsa + m, lds_addr(stage + Lds<SH>::SA + wave * 256));
     } else if (KIND == 1 && wave < SA_INS + SB_INS) {
         const int w = wave - SA_INS;
         int64_t n = T.n0 + w * 64 + lane;
         n = n < T.n_end ? n : T.n_end - 1;
-        dma4(T.sb + g * T.sb_s0 + n, lds_addr(stage + Lds<ACC>::SB + w * 256));
+        dma4(T.sb + g * T.sb_s0 + n, lds_addr(stage + Lds<SH>::SB + w * 256));
     } else if (KIND == 0 && wave == SA_INS && lane < BN / 128) {
         int64_t blk = (T.n0 >> 7) + lane;
         const int64_t last = (T.n_end - 1) >> 7;
         blk = blk < last ? blk : last;
-        dma4(T.sb + blk * T.sb_s0 + g * T.sb_s1, lds_addr(stage + Lds<ACC>::SB));
+        dma4(T.sb + blk * T.sb_s0 + g * T.sb_s1, lds_addr(stage + Lds<SH>::SB));
     }
 }
 
@@ -232,13 +230,13 @@ __device__ __forceinline__ void f16_pair(const uint8_t* tile, int row, int chunk
 
 // acc[i][j]: 32x32 sub-tile (m-sub i, n-sub j) of this wave, D^T layout:
 // register r of lane l is n = 32j + 8(r/4) + 4(l/32) + r%4, m = 32i + l%32.
-template <int KIND>
+template <int SH, int KIND>
 __device__ __forceinline__ void compute_f32(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
                                             int lane, int m_valid, v16f (&acc)[2][2]) {
-    const uint8_t* la = stage + Lds<0>::A;
-    const uint8_t* lb = stage + Lds<0>::B;
-    const float* lsa = (const float*)(stage + Lds<0>::SA);
-    const float* lsb = (const float*)(stage + Lds<0>::SB);
+    const uint8_t* la = stage + Lds<SH>::A;
+    const uint8_t* lb = stage + Lds<SH>::B;
+    const float* lsa = (const float*)(stage + Lds<SH>::SA);
+    const float* lsb = (const float*)(stage + Lds<SH>::SB);
     const int mbase = wm * 64, nbase = wn * 64;
     if (mbase >= m_valid) return;  // this wave's rows are all past the end
     const float sbk = KIND == 0 ? lsb[nbase >> 7] : 0.f;
@@ -287,6 +285,98 @@ __device__ __forceinline__ void compute_f32(const uint8_t* stage, const Tile& T,
     }
 }
 
+// Block-scale kind, software-pipelined: the fragments of k-chunk q+1 are
+// read from LDS while chunk q is widened and multiplied, and the partials
+// of the previous group are promoted at the start of this group, each
+// sub-tile's promotion just before the first MFMA that reuses its
+// registers, so the promotion FMAs run beside this group's MFMAs.  p and cp
+// carry the previous group's partials and scale factors (zero before the
+// first group).
+__device__ __forceinline__ uint4 lds16(const uint8_t* tile, int row, int chunk) {
+    return *(const uint4*)(tile + f8_off(row, chunk));
+}
+
+__device__ __forceinline__ void widen16(const uint4 v, v8h& lo, v8h& hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    v2h h[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        h[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        h[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        lo[2 * i] = h[i][0];
+        lo[2 * i + 1] = h[i][1];
+        hi[2 * i] = h[4 + i][0];
+        hi[2 * i + 1] = h[4 + i][1];
+    }
+}
+
+template <int SH>
+__device__ __forceinline__ void compute_f32_block(const uint8_t* stage, int wm, int wn, int lane,
+                                                  v16f (&acc)[2][2], v16f (&p)[2][2], float (&cp)[2]) {
+    const uint8_t* la = stage + Lds<SH>::A;
+    const uint8_t* lb = stage + Lds<SH>::B;
+    const float* lsa = (const float*)(stage + Lds<SH>::SA);
+    const float* lsb = (const float*)(stage + Lds<SH>::SB);
+    const int mbase = wm * 64, nbase = wn * 64;
+    const int r = lane & 31, h = lane >> 5;
+
+    uint4 ra[2], rb[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) ra[i] = lds16(la, mbase + 32 * i + r, h);
+#pragma unroll
+    for (int j = 0; j < 2; j++) rb[j] = lds16(lb, nbase + 32 * j + r, h);
+    const float sbk = lsb[nbase >> 7];
+    float cn[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) cn[i] = lsa[mbase + 32 * i + r] * sbk;
+
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint4 na[2], nb[2];
+        if (q < 3) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) na[i] = lds16(la, mbase + 32 * i + r, 2 * (q + 1) + h);
+#pragma unroll
+            for (int j = 0; j < 2; j++) nb[j] = lds16(lb, nbase + 32 * j + r, 2 * (q + 1) + h);
+        }
+        v8h a0[2], a1[2], b0[2], b1[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) widen16(ra[i], a0[i], a1[i]);
+#pragma unroll
+        for (int j = 0; j < 2; j++) widen16(rb[j], b0[j], b1[j]);
+        if (q == 0) {
+            const v16f zero = {};
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    acc[i][j] += p[i][j] * cp[i];
+                    p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], zero, 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], p[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], p[i][j], 0, 0, 0);
+        if (q < 3) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) ra[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < 2; j++) rb[j] = nb[j];
+        }
+    }
+    cp[0] = cn[0];
+    cp[1] = cn[1];
+}
+
 // ==== ACC_MFMA8 path: FP8 matrix cores, one MFMA per K group =============================
 //
 // Lane l feeds bytes [32(l/16), 32(l/16)+32) of its row: chunks 2(l/16) and
@@ -309,13 +399,13 @@ __device__ __forceinline__ v4f mfma8_group(const v8i& a, const v8i& b) {
 
 // acc[i][j]: 16x16 sub-tile (m-sub i, n-sub j), D^T layout: register e of
 // lane l is n = 16j + 4(l/16) + e, m = 16i + l%16.
-template <int KIND>
+template <int SH, int KIND>
 __device__ __forceinline__ void compute_mfma8(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
                                               int lane, int m_valid, v4f (&acc)[4][4]) {
-    const uint8_t* la = stage + Lds<1>::A;
-    const uint8_t* lb = stage + Lds<1>::B;
-    const float* lsa = (const float*)(stage + Lds<1>::SA);
-    const float* lsb = (const float*)(stage + Lds<1>::SB);
+    const uint8_t* la = stage + Lds<SH>::A;
+    const uint8_t* lb = stage + Lds<SH>::B;
+    const float* lsa = (const float*)(stage + Lds<SH>::SA);
+    const float* lsb = (const float*)(stage + Lds<SH>::SB);
     const int mbase = wm * 64, nbase = wn * 64;
     const int c0 = 2 * (lane >> 4);
     if (mbase >= m_valid) return;
@@ -411,14 +501,14 @@ __device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& 
 
 // ==== one tile: pipelined K loop, then the store ==============================================
 
-template <int ACC, int KIND, int OUT_F32>
+template <int ACC, int SH, int KIND, int OUT_F32>
 __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, void* d, int64_t ldd,
                                          uint8_t* smem) {
-    constexpr int S = Cfg<ACC>::STAGES;
+    constexpr int S = Shape<SH>::STAGES;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave % Cfg<ACC>::WGM, wn = wave / Cfg<ACC>::WGM;
-    const int m_valid = (int)(T.m_end - T.m0 < Cfg<ACC>::BM ? T.m_end - T.m0 : Cfg<ACC>::BM);
+    const int wm = wave % Shape<SH>::WGM, wn = wave / Shape<SH>::WGM;
+    const int m_valid = (int)(T.m_end - T.m0 < Shape<SH>::BM ? T.m_end - T.m0 : Shape<SH>::BM);
 
     typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;
     AccT acc;
@@ -436,14 +526,24 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
             for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
+    // pipelined block-kind f16 path: previous group's partials and factors
+    v16f pp[2][2];
+    float cp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) pp[i][j][r] = 0.f;
+
     // prologue: groups g0 .. g0+S-2
 #pragma unroll
     for (int s = 0; s < S - 1; s++)
-        if (g0 + s < g1) issue_stage<ACC, KIND>(T, g0 + s, smem + s * Lds<ACC>::STAGE, wave, lane);
+        if (g0 + s < g1) issue_stage<SH, KIND>(T, g0 + s, smem + s * Lds<SH>::STAGE, wave, lane);
 
     // Tile loads per group per wave; waves that also load scales issue one
     // more, so waiting for PER outstanding is conservative for them.
-    constexpr int PER = (Cfg<ACC>::BM + Cfg<ACC>::BN) / 8 / WAVES;
+    constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / WAVES;
     static_assert(S == 2 || (S == 3 && PER == 6), "wait counts cover these pipelines");
     for (int64_t g = g0; g < g1; g++) {
         const int64_t it = g - g0;
@@ -454,12 +554,21 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         else
             wait_and_barrier<0>();
         if (g + S - 1 < g1)
-            issue_stage<ACC, KIND>(T, g + S - 1, smem + ((it + S - 1) % S) * Lds<ACC>::STAGE, wave, lane);
-        const uint8_t* stage = smem + (it % S) * Lds<ACC>::STAGE;
-        if constexpr (ACC == 0)
-            compute_f32<KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
-        else
-            compute_mfma8<KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+            issue_stage<SH, KIND>(T, g + S - 1, smem + ((it + S - 1) % S) * Lds<SH>::STAGE, wave, lane);
+        const uint8_t* stage = smem + (it % S) * Lds<SH>::STAGE;
+        if constexpr (ACC == 0 && KIND == 0) {
+            if (wm * 64 < m_valid) compute_f32_block<SH>(stage, wm, wn, lane, acc, pp, cp);
+        } else if constexpr (ACC == 0) {
+            compute_f32<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+        } else {
+            compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+        }
+    }
+    if constexpr (ACC == 0 && KIND == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) acc[i][j] += pp[i][j] * cp[i];
     }
     wait_and_barrier<0>();  // the LDS stages may be reused by a following tile
 
@@ -473,7 +582,7 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
 
 template <int ACC, int KIND, int OUT_F32, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<ACC>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t ntiles = tiles_m * tiles_n;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t split = SPLIT ? wid / ntiles : 0;
@@ -481,9 +590,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
     tile_coords(wid % ntiles, tiles_m, tiles_n, tm, tn);
 
     Tile T;
-    T.m0 = tm * Cfg<ACC>::BM;
+    T.m0 = tm * Shape<0>::BM;
     T.m_end = p.M;
-    T.n0 = tn * Cfg<ACC>::BN;
+    T.n0 = tn * Shape<0>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -500,16 +609,16 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
         const int64_t per = (groups + p.splits - 1) / p.splits;
         const int64_t g0 = split * per;
         const int64_t g1 = g0 + per < groups ? g0 + per : groups;
-        run_tile<ACC, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
+        run_tile<ACC, 0, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
     } else {
-        run_tile<ACC, KIND, OUT_F32>(T, 0, groups, p.d, p.ldd, smem);
+        run_tile<ACC, 0, KIND, OUT_F32>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
 
 // Grouped: workgroup (expert e, n-tile) walks the expert's m-tiles.
 template <int ACC, int OUT_F32>
 __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<ACC>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t e = wid / tiles_n;
     const int64_t tn = wid % tiles_n;
@@ -517,7 +626,7 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
 
     Tile T;
     T.m_end = r1;
-    T.n0 = tn * Cfg<ACC>::BN;
+    T.n0 = tn * Shape<0>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -528,9 +637,9 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     T.sb = p.sb + e * p.sb_estride;
     T.sb_s0 = p.K / 128;
     T.sb_s1 = 1;
-    for (int64_t m0 = r0; m0 < r1; m0 += Cfg<ACC>::BM) {
+    for (int64_t m0 = r0; m0 < r1; m0 += Shape<0>::BM) {
         T.m0 = m0;
-        run_tile<ACC, 0, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
+        run_tile<ACC, 0, 0, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
     }
 }
 
@@ -556,10 +665,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ==== host side ==========================================================================
 
-// The split count is chosen from the f16-path tile (the smaller one) so the
-// workspace query does not depend on the accumulation mode.
 int gemm_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + Cfg<0>::BM - 1) / Cfg<0>::BM) * ((N + Cfg<0>::BN - 1) / Cfg<0>::BN);
+    const int64_t tiles = ((M + Shape<0>::BM - 1) / Shape<0>::BM) * ((N + Shape<0>::BN - 1) / Shape<0>::BN);
     const int64_t groups = K / 128;
     if (tiles == 0 || groups < 16 || tiles >= 128) return 1;
     int64_t s = 256 / tiles;         // about one workgroup per CU
@@ -583,8 +690,8 @@ static void launch_dense(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, in
 
 template <int ACC>
 static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
-    const int64_t tiles_m = (g.M + Cfg<ACC>::BM - 1) / Cfg<ACC>::BM;
-    const int64_t tiles_n = (g.N + Cfg<ACC>::BN - 1) / Cfg<ACC>::BN;
+    const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
+    const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     if (g.splits > 1) {
         const int64_t wgs = tiles_m * tiles_n * g.splits;
         if (g.bscale_kind == 0)
@@ -625,7 +732,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 template <int ACC>
 static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
-    const int64_t tiles_n = (g.N + Cfg<ACC>::BN - 1) / Cfg<ACC>::BN;
+    const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     const dim3 grid((unsigned)(tiles_n * g.G));
     if (g.out_f32)
         hipLaunchKernelGGL((grouped_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);

@@ -18,6 +18,14 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int
                               uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
                               int64_t lds, hipStream_t st);
 
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool pow2, uint8_t* qr,
+                             int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc, float* sc,
+                             int64_t ldsc, hipStream_t st);
+
+hipError_t launch_requant_col(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                              int64_t lds, bool pow2, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                              hipStream_t st_);
+
 // Everything a block-scaled GEMM launch needs.  For a grouped launch,
 // `offsets` is non-null, `G` experts share N and K, expert e's codes start at
 // b + e*b_estride and its block scales at sb + e*sb_estride.

@@ -255,6 +255,155 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
     block_finish<POW2>(v, wmax, rows, bi, bj, r0, c0, q, ldq, qt, ldqt, s, lds);
 }
 
+// ---- both orientations from one read -------------------------------------------------------
+//
+// The backward pass needs dY in 1x128 groups (Dgrad) and in 128x1 groups
+// (Wgrad).  A workgroup covers one 128 x 128 tile of x, read once.  Pass p,
+// wave w, 16-lane DPP row d: lanes read rows r = 32p + 8w + 2d and r + 1 (16 B
+// of bf16 each), quantise both as 1x128 groups (each row of the tile is one
+// group), and store the two rows' values of every column packed in one
+// dword of a column-major LDS tile (row pair r/2; the 16-byte chunk index
+// XOR-swizzled by c/8, so the 64 lanes of a store hit distinct banks).  After
+// the barrier each DPP row quantises one column at a time as a 128x1 group,
+// as quant_col_kernel does.
+
+__device__ __forceinline__ uint32_t dual_lds_index(int c, int rp) {
+    return (uint32_t)(c * 64 + ((((rp >> 2) ^ (c >> 3)) & 15) << 2) + (rp & 3));
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                         uint8_t* __restrict__ qr, int64_t ldqr,
+                                                         float* __restrict__ sr, int64_t ldsr,
+                                                         uint8_t* __restrict__ qc, int64_t ldqc,
+                                                         float* __restrict__ sc, int64_t ldsc,
+                                                         int64_t col_tiles) {
+    __shared__ uint32_t tile[128 * 64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l = lane & 15, d = lane >> 4;
+    const int64_t g = blockIdx.x / col_tiles;
+    const int64_t c0 = (blockIdx.x % col_tiles) * 128;
+    const int64_t gc = c0 >> 7;
+
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int64_t r = g * 128 + 32 * p + 8 * wave + 2 * d;
+        a[p] = ld_stream16(x + r * ldx + c0 + 8 * l);
+        b[p] = ld_stream16(x + (r + 1) * ldx + c0 + 8 * l);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int64_t r = g * 128 + 32 * p + 8 * wave + 2 * d;
+        const GroupScale ga = group_scale(row16_max(absmax8(a[p])), POW2);
+        const GroupScale gb = group_scale(row16_max(absmax8(b[p])), POW2);
+        st_stream8(qr + r * ldqr + c0 + 8 * l, quant8(a[p], ga.inv));
+        st_stream8(qr + (r + 1) * ldqr + c0 + 8 * l, quant8(b[p], gb.inv));
+        if (l == 0) {
+            sr[gc * ldsr + r] = ga.s;
+            sr[gc * ldsr + r + 1] = gb.s;
+        }
+        const int rp = 16 * p + 4 * wave + d;
+        const uint32_t wa[4] = {a[p].x, a[p].y, a[p].z, a[p].w};
+        const uint32_t wb[4] = {b[p].x, b[p].y, b[p].z, b[p].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c = 8 * l + 2 * j;
+            tile[dual_lds_index(c, rp)] = perm(wb[j], wa[j], 0x05040100u);
+            tile[dual_lds_index(c + 1, rp)] = perm(wb[j], wa[j], 0x07060302u);
+        }
+    }
+    __syncthreads();
+
+#pragma unroll 2
+    for (int it = 0; it < 8; it++) {
+        const int c = wave * 32 + it * 4 + d;
+        const uint4 v = *(const uint4*)&tile[dual_lds_index(c, 4 * l)];
+        const GroupScale gs = group_scale(row16_max(absmax8(v)), POW2);
+        st_stream8(qc + (c0 + c) * ldqc + g * 128 + 8 * l, quant8(v, gs.inv));
+        if (l == 0) sc[g * ldsc + c0 + c] = gs.s;
+    }
+}
+
+// ---- backward re-tiling: 1x128 codes -> 128x1 codes ------------------------------------
+//
+// A workgroup covers one 128 x 128 tile, whose 128 columns share one 1x128
+// scale per row.  Thread t reads the 8 x 8 code block at rows 8(t/16)..,
+// columns 8(t%16).. (16 lanes read a row's 128 B), transposes it in
+// registers and stores it column-major in LDS: column c holds its 128
+// codes as 16 chunks of 8 rows, chunk index XOR-swizzled by c/8 so the 16
+// lanes of a store hit distinct banks.  Then each 16-lane DPP row takes one
+// column at a time: lane l dequantises rows 8l..8l+7 (exact decode, then
+// one fp32 multiply by the row's scale), the row reduces the column's
+// amax, and the 16 lanes write the 128 new codes as one 128-byte run of
+// the transposed output.
+
+// Exact values of the four E4M3 codes packed in a dword (low byte first).
+__device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    v[0] = (float)lo[0];
+    v[1] = (float)lo[1];
+    v[2] = (float)hi[0];
+    v[3] = (float)hi[1];
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void requant_col_kernel(const uint8_t* __restrict__ q, int64_t ldq,
+                                                          const float* __restrict__ s, int64_t lds,
+                                                          uint8_t* __restrict__ qt, int64_t ldqt,
+                                                          float* __restrict__ st, int64_t ldst,
+                                                          int64_t col_tiles) {
+    __shared__ uint2 tile[128 * 16];
+    const int t = threadIdx.x;
+    const int64_t g = blockIdx.x / col_tiles;
+    const int64_t c0 = (blockIdx.x % col_tiles) * 128;
+    {
+        const int rb = t >> 4, cb = t & 15;
+        const uint8_t* src = q + (g * 128 + 8 * rb) * ldq + c0 + 8 * cb;
+        uint2 r[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const u32x2 w = __builtin_nontemporal_load((const u32x2*)(src + i * ldq));
+            r[i] = make_uint2(w.x, w.y);
+        }
+        uint32_t lo[8], hi[8];  // column j: rows 0-3 in lo[j], rows 4-7 in hi[j]
+        transpose4x4(r[0].x, r[1].x, r[2].x, r[3].x, lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4(r[4].x, r[5].x, r[6].x, r[7].x, hi[0], hi[1], hi[2], hi[3]);
+        transpose4x4(r[0].y, r[1].y, r[2].y, r[3].y, lo[4], lo[5], lo[6], lo[7]);
+        transpose4x4(r[4].y, r[5].y, r[6].y, r[7].y, hi[4], hi[5], hi[6], hi[7]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) tile[(8 * cb + j) * 16 + (rb ^ cb)] = make_uint2(lo[j], hi[j]);
+    }
+    const int lane = t & 63, wave = t >> 6, l = lane & 15;
+    const float* sp = s + (c0 >> 7) * lds + g * 128 + 8 * l;
+    const float4 sa = *(const float4*)sp, sb = *(const float4*)(sp + 4);
+    const float rs[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    __syncthreads();
+
+#pragma unroll 2
+    for (int it = 0; it < 8; it++) {
+        const int c = wave * 32 + it * 4 + (lane >> 4);
+        const uint2 v = tile[c * 16 + (l ^ (c >> 3))];
+        float x[8], d[4];
+        decode4(v.x, d);
+#pragma unroll
+        for (int i = 0; i < 4; i++) x[i] = d[i] * rs[i];
+        decode4(v.y, d);
+#pragma unroll
+        for (int i = 0; i < 4; i++) x[4 + i] = d[i] * rs[4 + i];
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+        am = row16_max(am);
+        const GroupScale gs = group_scale(am, POW2);
+        const uint2 codes = make_uint2(pack4(x[0] * gs.inv, x[1] * gs.inv, x[2] * gs.inv, x[3] * gs.inv),
+                                       pack4(x[4] * gs.inv, x[5] * gs.inv, x[6] * gs.inv, x[7] * gs.inv));
+        st_stream8(qt + (c0 + c) * ldqt + g * 128 + 8 * l, codes);
+        if (l == 0) st[g * ldst + c0 + c] = gs.s;
+    }
+}
+
 // ---- launchers -------------------------------------------------------------------------------
 
 hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
@@ -290,6 +439,34 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int
         hipLaunchKernelGGL(quant_block_kernel<true>, grid, dim3(256), 0, st, w, rows, ldw, q, ldq, qt, ldqt, s, lds, cb);
     else
         hipLaunchKernelGGL(quant_block_kernel<false>, grid, dim3(256), 0, st, w, rows, ldw, q, ldq, qt, ldqt, s, lds, cb);
+    return hipGetLastError();
+}
+
+hipError_t launch_requant_col(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                              int64_t lds, bool pow2, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                              hipStream_t st_) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t ct = cols / 128, gt = rows / 128;
+    const dim3 grid((unsigned)(ct * gt));
+    if (pow2)
+        hipLaunchKernelGGL(requant_col_kernel<true>, grid, dim3(256), 0, st_, q, ldq, s, lds, qt, ldqt, st, ldst, ct);
+    else
+        hipLaunchKernelGGL(requant_col_kernel<false>, grid, dim3(256), 0, st_, q, ldq, s, lds, qt, ldqt, st, ldst, ct);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool pow2, uint8_t* qr,
+                             int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc, float* sc,
+                             int64_t ldsc, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t ct = cols / 128, gt = rows / 128;
+    const dim3 grid((unsigned)(ct * gt));
+    if (pow2)
+        hipLaunchKernelGGL(quant_dual_kernel<true>, grid, dim3(256), 0, st, x, ldx, qr, ldqr, sr, ldsr, qc, ldqc, sc,
+                           ldsc, ct);
+    else
+        hipLaunchKernelGGL(quant_dual_kernel<false>, grid, dim3(256), 0, st, x, ldx, qr, ldqr, sr, ldsr, qc, ldqc, sc,
+                           ldsc, ct);
     return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 2
+#define FP8BS_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -169,6 +169,58 @@ int fp8_quant_block(const uint16_t *w, int64_t rows, int64_t cols,
                     int64_t ldw, int scale_mode, uint8_t *q, int64_t ldq,
                     uint8_t *qt, int64_t ldqt, float *s, int64_t lds,
                     void *stream);
+
+/*
+ * fp8_quant_dual -- both activation groupings from one read of x: the 1x128
+ * groups (as fp8_quant_tile with FP8BS_AXIS_ROW) and the 128x1 groups (as
+ * FP8BS_AXIS_COL), for a gradient that feeds both Dgrad and Wgrad
+ * ([hacks-368261], passage on the backward pass needing 128x1 tiles next
+ * to the 1x128 tiles, and on the HBM round trips quantisation costs).
+ * Outputs equal the two fp8_quant_tile calls bit for bit.
+ *
+ *   x      bf16 bits [rows][ldx]; rows and cols multiples of 128.
+ *   qr, sr the ROW outputs: qr [rows][ldqr], sr[g*ldsr + r].
+ *   qc, sc the COL outputs: qc [cols][ldqc] (transposed), sc[g*ldsc + c].
+ *
+ * Alignment: x, qr, qc 16-byte aligned; ldx a multiple of 8; ldqr and ldqc
+ * multiples of 16; sr, sc 4-byte aligned.  ldx, ldqr >= cols; ldqc >= rows;
+ * ldsr >= rows; ldsc >= cols.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_quant_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                   int scale_mode, uint8_t *qr, int64_t ldqr, float *sr,
+                   int64_t ldsr, uint8_t *qc, int64_t ldqc, float *sc,
+                   int64_t ldsc, void *stream);
+
+/*
+ * fp8_requant_col -- backward re-tiling ([hacks-368261], passage on the
+ * backward pass reading the FP8 activations back, dequantising them,
+ * transposing them and re-quantising them into 128x1 tiles).
+ *
+ *   q     codes [rows][ldq] quantised in 1x128 row groups, with
+ *   s     their scales s[g*lds + r] (g < cols/128) -- the layout
+ *         fp8_quant_tile writes for FP8BS_AXIS_ROW.
+ *   The matrix is dequantised element by element as the fp32 product
+ *   x = decode(q) * s (one rounding), transposed, and quantised again in
+ *   128x1 groups down its columns with `scale_mode`:
+ *   qt    codes [cols][ldqt], written TRANSPOSED: qt[c][128g + i] encodes
+ *         x[128g + i][c];
+ *   st    st[g*ldst + c] is the scale of group (g, c), g < rows/128 -- the
+ *         layout fp8_quant_tile writes for FP8BS_AXIS_COL.
+ *   rows and cols must be multiples of 128.  The dequantised values must be
+ *   finite fp32: codes 0x7F / 0xFF (NaN, never produced by the quantisers)
+ *   and power-of-two scales of groups whose amax lies within 1/16 of the
+ *   fp32 maximum (their largest code times the scale overflows) are
+ *   outside the contract.
+ *
+ * Alignment: q and qt 16-byte aligned, ldq and ldqt multiples of 16; s
+ * 16-byte aligned with lds a multiple of 4; st 4-byte aligned.  ldq >= cols,
+ * lds >= rows, ldqt >= rows, ldst >= cols.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                    const float *s, int64_t lds, int scale_mode, uint8_t *qt,
+                    int64_t ldqt, float *st, int64_t ldst, void *stream);
 
 /*
  * fp8_gemm_blockscaled -- block-scaled FP8 GEMM with FP32 promotion every

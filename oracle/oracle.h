@@ -80,7 +80,7 @@ int orc_quant_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ldw,
  * dequantised (x = fl32(dec(q) * s)), transposed and quantised again in
  * 128x1 groups down its columns: qt [cols][ldqt], scale of group g of column
  * c in st[g*ldst + c] (the layout of axis 1).  rows and cols must be
- * multiples of 128. */
+ * multiples of 128; the dequantised values must be finite in fp32. */
 int orc_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
                     const float *s, int64_t lds, int pow2, uint8_t *qt,
                     int64_t ldqt, float *st, int64_t ldst);

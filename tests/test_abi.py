@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
+    for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -44,7 +44,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bs.abi_version() == 2
+    assert bs.abi_version() == 3
     for s in range(7):
         assert bs.status_string(s)
     assert "unknown" in bs.status_string(99)
@@ -83,6 +83,44 @@ def _block(**kw):
 ])
 def test_quant_block_validation(kw, want):
     assert _block(**kw) == want
+
+
+def _dual(**kw):
+    a = dict(x=FAKE, rows=256, cols=384, ldx=384, mode=0, qr=FAKE, ldqr=384, sr=FAKE, ldsr=256, qc=FAKE,
+             ldqc=256, sc=FAKE, ldsc=384)
+    a.update(kw)
+    return bs.lib().fp8_quant_dual(a["x"], a["rows"], a["cols"], a["ldx"], a["mode"], a["qr"], a["ldqr"],
+                                   a["sr"], a["ldsr"], a["qc"], a["ldqc"], a["sc"], a["ldsc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mode=2), ARG), (dict(x=None), ARG), (dict(qr=None), ARG), (dict(sc=None), ARG), (dict(cols=-128), ARG),
+    (dict(ldx=256), ARG), (dict(ldqr=256), ARG), (dict(ldqc=128), ARG), (dict(ldsr=128), ARG), (dict(ldsc=256), ARG),
+    (dict(rows=200, ldqc=256, ldsr=256), SHAPE), (dict(cols=200, ldx=384), SHAPE), (dict(x=FAKE + 8), ALIGN),
+    (dict(qc=FAKE + 4), ALIGN), (dict(sr=FAKE + 1), ALIGN), (dict(ldx=388), ALIGN), (dict(ldqc=264), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_dual_validation(kw, want):
+    assert _dual(**kw) == want
+
+
+def _requant(**kw):
+    a = dict(q=FAKE, rows=256, cols=384, ldq=384, s=FAKE, lds=256, mode=0, qt=FAKE, ldqt=256, st=FAKE, ldst=384)
+    a.update(kw)
+    return bs.lib().fp8_requant_col(a["q"], a["rows"], a["cols"], a["ldq"], a["s"], a["lds"], a["mode"],
+                                    a["qt"], a["ldqt"], a["st"], a["ldst"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mode=2), ARG), (dict(q=None), ARG), (dict(s=None), ARG), (dict(qt=None), ARG), (dict(st=None), ARG),
+    (dict(rows=-128), ARG), (dict(ldq=256), ARG), (dict(lds=128), ARG), (dict(ldqt=128), ARG),
+    (dict(ldst=256), ARG), (dict(rows=200, lds=256, ldqt=256), SHAPE), (dict(cols=200, ldq=384), SHAPE),
+    (dict(q=FAKE + 8), ALIGN), (dict(qt=FAKE + 4), ALIGN), (dict(s=FAKE + 4), ALIGN), (dict(st=FAKE + 2), ALIGN),
+    (dict(ldq=392), ALIGN), (dict(ldqt=264), ALIGN), (dict(lds=258), ALIGN),
+    (dict(rows=0), OK), (dict(cols=0, ldq=0, ldst=0), OK),
+])
+def test_requant_validation(kw, want):
+    assert _requant(**kw) == want
 
 
 def _gemm(**kw):
