@@ -2,6 +2,18 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum fp32|mfma8]
     python bench.py --traffic-probe     # plain copy of known size, for counter scaling
+    python bench.py --workload expert_backward|grouped_upproj|decode_grouped
+
+The default line (--workload dense_fprop) is the headline measurement.  The
+other workloads print one JSON line of the same form for the other shapes
+the path is measured on (no CPU baseline):
+  expert_backward: dY[8192x2048] quantised both ways in one pass, X's 1x128
+    forward codes re-tiled to 128x1, Dgrad 8192x7168x2048 and Wgrad
+    2048x7168x8192, fp32 out (W's transposed codes come from the forward);
+  grouped_upproj: 32 local experts of a top-8-of-256 routing of 4096 tokens,
+    quant X 1x128 + quant W[32x4096x7168] 128x128 (power-of-two scales) +
+    grouped GEMM, bf16 out;
+  decode_grouped: 64 experts with 1..256 rows, N = 2048, same steps.
 
 Workload: the dense Fprop at real width -- X[4096 x 7168] bf16 ~N(0,1) with
 0.1% x100 outliers, W[18432 x 7168] bf16 ~N(0,0.02).  One step is the whole
@@ -117,6 +129,119 @@ def cpu_baseline(X, W, target_s=20.0):
                       f"(quant 1x128 + quant 128x128 + GEMM {ms}x{ns}x{K}), {dt:.1f} s"}
 
 
+PEAK_UNIT = {"TFLOP/s": (PEAK_FP8_TFLOPS, "mfma"), "GB/s": (PEAK_HBM_GBPS, "hbm")}
+
+
+def time_steps(step_fns, steps, warmup):
+    """Run the kernels of a step `warmup` times, then `steps` times with a HIP
+    event around each (events on torch's current stream, which the binding
+    passes to the library).  Returns (ms per step from the host clock,
+    [mean ms per kernel])."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in step_fns:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step_fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        for j, (_, fn) in enumerate(step_fns):
+            fn()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(len(step_fns))]
+    return wall, per
+
+
+def other_workload(name, args):
+    """The non-default workloads (see the module docstring)."""
+    import torch
+    import block_scaled_gemm_amd as bs
+    from block_scaled_gemm_amd import inputs
+    dev = torch.device("cuda:0")
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8}[args.accum]
+    kernels = []  # (name, fn, work, unit)
+    if name == "expert_backward":
+        d = inputs.expert_backward()
+        dY, X, W = to_bf16(d["dY"]), to_bf16(d["X"]), to_bf16(d["W"])
+        T, Nw, Kw = 8192, 2048, 7168
+        # forward-pass products the backward pass starts from
+        qx, sx = bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_FP32)
+        _, sw, qwt = bs.fp8_quant_block(W, bs.SCALE_FP32, transpose=True)
+        del X, W
+        out = {}
+        dx = torch.empty((T, Kw), dtype=torch.float32, device=dev)
+        dw = torch.empty((Nw, Kw), dtype=torch.float32, device=dev)
+        qxt = torch.empty((Kw, T), dtype=torch.uint8, device=dev)
+        sxt = torch.empty((T // 128, Kw), dtype=torch.float32, device=dev)
+
+        def dual():
+            out["qr"], out["sr"], out["qc"], out["sc"] = bs.fp8_quant_dual(dY, bs.SCALE_FP32)
+        kernels = [
+            ("quant_dual dY[8192x2048]", dual, T * Nw * 4 + 2 * (T * Nw // 128) * 4, "GB/s"),
+            ("requant_col X[8192x7168]", lambda: bs.fp8_requant_col(qx, sx, bs.SCALE_FP32, qt=qxt, st=sxt),
+             T * Kw * 2 + 2 * (T * Kw // 128) * 4, "GB/s"),
+            ("dgrad 8192x7168x2048", lambda: bs.fp8_gemm_blockscaled(
+                out["qr"], out["sr"], qwt, sw, bs.BSCALE_BLOCK, 1, sw.stride(0), bs.OUT_F32, d=dx, accum=accum),
+             2.0 * T * Kw * Nw / 1e3, "TFLOP/s"),
+            ("wgrad 2048x7168x8192", lambda: bs.fp8_gemm_blockscaled(
+                out["qc"], out["sc"], qxt, sxt, bs.BSCALE_TILE, sxt.stride(0), 0, bs.OUT_F32, d=dw, accum=accum),
+             2.0 * Nw * Kw * T / 1e3, "TFLOP/s"),
+        ]
+        flops = 4.0 * T * Kw * Nw
+        config = {"workload": "expert backward: quant dY[8192x2048] 1x128 and 128x1 in one pass + re-tile "
+                              "X[8192x7168] 1x128 -> 128x1 + Dgrad 8192x7168x2048 + Wgrad 2048x7168x8192 -> fp32"}
+    else:
+        d = inputs.grouped_upproj() if name == "grouped_upproj" else inputs.decode_grouped()
+        G, N, K = d["W"].shape
+        offsets = torch.from_numpy(d["offsets"]).to(dev)
+        rows = int(d["offsets"][-1])
+        Xc, Wc = to_bf16(d["Xcat"]), to_bf16(d["W"].reshape(G * N, K))
+        mode = bs.SCALE_POW2 if name == "grouped_upproj" else bs.SCALE_FP32
+        qx = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        sx = torch.empty((K // 128, rows), dtype=torch.float32, device=dev)
+        qw = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+        sw = torch.empty((G * N // 128, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+        kernels = [
+            (f"quant_tile X[{rows}x{K}]", lambda: bs.fp8_quant_tile(Xc, bs.AXIS_ROW, mode, q=qx, s=sx),
+             quant_bytes_row(rows, K), "GB/s"),
+            (f"quant_block W[{G}x{N}x{K}]", lambda: bs.fp8_quant_block(Wc, mode, q=qw, s=sw),
+             quant_bytes_block(G * N, K), "GB/s"),
+            (f"grouped GEMM G={G} rows={rows} N={N} K={K}", lambda: bs.fp8_grouped_gemm(
+                offsets, qx, sx, qw.view(G, N, K), sw.view(G, N // 128, K // 128), bs.OUT_BF16, d=y, accum=accum),
+             2.0 * rows * N * K / 1e3, "TFLOP/s"),
+        ]
+        flops = 2.0 * rows * N * K
+        config = {"workload": f"{name}: quant X[{rows}x{K}] 1x128 + quant W[{G}x{N}x{K}] 128x128 + grouped "
+                              f"GEMM ({G} experts, {rows} rows, N={N}, K={K}) -> bf16",
+                  "scales": "pow2" if mode == bs.SCALE_POW2 else "fp32"}
+    config["accum"] = args.accum
+    wall, per = time_steps([(k[0], k[1]) for k in kernels], args.steps, args.warmup)
+    report = {}
+    for (kname, _, work, unit), ms in zip(kernels, per):
+        ach = work / (ms * 1e-3) / 1e9  # GB/s for bytes, TFLOP/s for flops / 1e3
+        peak, _ = PEAK_UNIT[unit]
+        report[kname] = {"ms": ms, unit: ach, "frac": ach / peak}
+    dom = int(np.argmax(per))
+    kname, _, work, unit = kernels[dom]
+    peak, bound = PEAK_UNIT[unit]
+    ach = report[kname][unit]
+    print(json.dumps({
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% MFMA peak); quantize GB/s (% HBM peak)",
+        "value": flops / (wall * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded numpy, shapes and distributions of the workload)",
+        "config": config,
+        "roofline": {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                     "traffic": None, "kernel": kname, "kernel_ms": per[dom]},
+        "kernels": report, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +252,8 @@ def main():
                     help="GEMM accumulation: exact group partials (fp32) or FP8 matrix cores (mfma8)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only a plain copy of known size (counter scaling)")
+    ap.add_argument("--workload", default="dense_fprop",
+                    choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "
@@ -135,6 +262,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.workload != "dense_fprop":
+        other_workload(args.workload, args)
         return
 
     import torch
