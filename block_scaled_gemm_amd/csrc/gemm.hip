@@ -104,6 +104,17 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gptr) : "memory");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the instruction's SADDR form): the per-lane offsets stay
+// fixed over the K loop and only the scalar base advances.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
 // Wait until at most N of this wave's direct loads are in flight, then
 // barrier.  The memory clobber keeps the compiler from moving LDS accesses
 // across it.
@@ -158,50 +169,69 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
 }
 
 // ---- staging: issue one K group of both tiles and their scales into a stage ---------------
+//
+// Per-lane source offsets are computed once per tile (rows past the end are
+// clamped to the last row, so every load stays inside the operand); per
+// group only the wave-uniform base pointers advance.  Each wave instruction
+// moves 8 rows of 128 B: lane i fetches chunk (i%8) ^ swz(row) of row i/8
+// and lands at LDS base + 16*i.
 
 template <int SH, int KIND>
-__device__ __forceinline__ void issue_stage(const Tile& T, int64_t g, uint8_t* stage, int wave, int lane) {
-    constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
-    const int64_t k0 = g * 128;
-    // A: BM/8 instructions of 8 rows, spread over the waves
+struct Stager {
+    static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
+    static constexpr int NA = BM / 8 / WAVES, NB = BN / 8 / WAVES;
+    static constexpr int SA_INS = BM / 64, SB_INS = BN / 64;
+    uint32_t va[NA], vb[NB], vs;
+
+    __device__ __forceinline__ void init(const Tile& T, int wave, int lane) {
 #pragma unroll
-    for (int ins = 0; ins < BM / 8 / WAVES; ins++) {
-        const int row0 = (ins * WAVES + wave) * 8;
-        const int row = row0 + (lane >> 3);
-        int64_t m = T.m0 + row;
-        m = m < T.m_end ? m : T.m_end - 1;
-        const uint8_t* src = T.a + m * T.lda + k0 + (((lane & 7) ^ swz(row)) << 4);
-        dma16(src, lds_addr(stage + Lds<SH>::A + row0 * 128));
-    }
+        for (int ins = 0; ins < NA; ins++) {
+            const int row = (ins * WAVES + wave) * 8 + (lane >> 3);
+            const int64_t m = T.m0 + row < T.m_end ? T.m0 + row : T.m_end - 1;
+            va[ins] = (uint32_t)((m - T.m0) * T.lda) + ((((lane & 7) ^ swz(row))) << 4);
+        }
 #pragma unroll
-    for (int ins = 0; ins < BN / 8 / WAVES; ins++) {
-        const int row0 = (ins * WAVES + wave) * 8;
-        const int row = row0 + (lane >> 3);
-        int64_t n = T.n0 + row;
-        n = n < T.n_end ? n : T.n_end - 1;
-        const uint8_t* src = T.b + n * T.ldb + k0 + (((lane & 7) ^ swz(row)) << 4);
-        dma16(src, lds_addr(stage + Lds<SH>::B + row0 * 128));
+        for (int ins = 0; ins < NB; ins++) {
+            const int row = (ins * WAVES + wave) * 8 + (lane >> 3);
+            const int64_t n = T.n0 + row < T.n_end ? T.n0 + row : T.n_end - 1;
+            vb[ins] = (uint32_t)((n - T.n0) * T.ldb) + ((((lane & 7) ^ swz(row))) << 4);
+        }
+        vs = 0;
+        if (wave < SA_INS) {
+            const int64_t m = T.m0 + wave * 64 + lane < T.m_end ? T.m0 + wave * 64 + lane : T.m_end - 1;
+            vs = (uint32_t)(m - T.m0) * 4;
+        } else if (KIND == 1 && wave < SA_INS + SB_INS) {
+            const int w = wave - SA_INS;
+            const int64_t n = T.n0 + w * 64 + lane < T.n_end ? T.n0 + w * 64 + lane : T.n_end - 1;
+            vs = (uint32_t)(n - T.n0) * 4;
+        }
     }
-    // scales: the first waves load sa (64 floats per instruction); the
-    // waves after them load the B scales -- BN per-column floats (tile
-    // kind) or the BN/128 block scalars of this group (block kind)
-    constexpr int SA_INS = BM / 64, SB_INS = BN / 64;
-    if (wave < SA_INS) {
-        int64_t m = T.m0 + wave * 64 + lane;
-        m = m < T.m_end ? m : T.m_end - 1;
-        dma4(T.sa + g * T.ldsa + m, lds_addr(stage + Lds<SH>::SA + wave * 256));
-    } else if (KIND == 1 && wave < SA_INS + SB_INS) {
-        const int w = wave - SA_INS;
-        int64_t n = T.n0 + w * 64 + lane;
-        n = n < T.n_end ? n : T.n_end - 1;
-        dma4(T.sb + g * T.sb_s0 + n, lds_addr(stage + Lds<SH>::SB + w * 256));
-    } else if (KIND == 0 && wave == SA_INS && lane < BN / 128) {
-        int64_t blk = (T.n0 >> 7) + lane;
-        const int64_t last = (T.n_end - 1) >> 7;
-        blk = blk < last ? blk : last;
-        dma4(T.sb + blk * T.sb_s0 + g * T.sb_s1, lds_addr(stage + Lds<SH>::SB));
+
+    // Group g into the stage at LDS byte offset `stage` of smem.
+    __device__ __forceinline__ void issue(const Tile& T, int64_t g, uint8_t* smem, int stage, int wave) const {
+        const uint8_t* a = T.a + T.m0 * T.lda + g * 128;
+        const uint8_t* b = T.b + T.n0 * T.ldb + g * 128;
+        const uint32_t base = lds_addr(smem + stage);
+#pragma unroll
+        for (int ins = 0; ins < NA; ins++)
+            dma16s(va[ins], a, base + Lds<SH>::A + (ins * WAVES + wave) * 8 * 128);
+#pragma unroll
+        for (int ins = 0; ins < NB; ins++)
+            dma16s(vb[ins], b, base + Lds<SH>::B + (ins * WAVES + wave) * 8 * 128);
+        // scales: the first waves load sa (64 floats per instruction); the
+        // waves after them load the B scales -- BN per-column floats (tile
+        // kind) or, block kind, the group's block scalar (every lane loads
+        // the same word; the BN/128 = 1 copies that matter sit first)
+        static_assert(KIND == 1 || BN == 128, "block kind stages one block scalar per group");
+        if (wave < SA_INS) {
+            dma4s(vs, T.sa + g * T.ldsa + T.m0, base + Lds<SH>::SA + wave * 256);
+        } else if (KIND == 1 && wave < SA_INS + SB_INS) {
+            dma4s(vs, T.sb + g * T.sb_s0 + T.n0, base + Lds<SH>::SB + (wave - SA_INS) * 256);
+        } else if (KIND == 0 && wave == SA_INS) {
+            dma4s(0u, T.sb + (T.n0 >> 7) * T.sb_s0 + g * T.sb_s1, base + Lds<SH>::SB);
+        }
     }
-}
+};
 
 // ==== ACC_F32 path: exact f16 widening, f16 matrix cores =============================
 //
@@ -536,26 +566,29 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
 #pragma unroll
             for (int r = 0; r < 16; r++) pp[i][j][r] = 0.f;
 
+    Stager<SH, KIND> stg;
+    stg.init(T, wave, lane);
     // prologue: groups g0 .. g0+S-2
 #pragma unroll
     for (int s = 0; s < S - 1; s++)
-        if (g0 + s < g1) issue_stage<SH, KIND>(T, g0 + s, smem + s * Lds<SH>::STAGE, wave, lane);
+        if (g0 + s < g1) stg.issue(T, g0 + s, smem, s * Lds<SH>::STAGE, wave);
 
     // Tile loads per group per wave; waves that also load scales issue one
     // more, so waiting for PER outstanding is conservative for them.
     constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / WAVES;
-    static_assert(S == 2 || (S == 3 && PER == 6), "wait counts cover these pipelines");
-    for (int64_t g = g0; g < g1; g++) {
-        const int64_t it = g - g0;
-        // group g has landed (at most the following group still in flight)
-        // for every wave, and every wave is done with the stage of g-1
-        if (S == 3 && g + 1 < g1)
+    static_assert(S == 3 && PER == 6, "wait counts cover this pipeline");
+    // One group: wait until it has landed (at most the following group
+    // still in flight) for every wave and every wave is done with the stage
+    // of the previous group, refill that stage, compute.  The stage index SS
+    // is a compile-time constant, so LDS addresses fold into immediates.
+    auto step = [&](auto ss, int64_t g) {
+        constexpr int SS = decltype(ss)::value;
+        if (g + 1 < g1)
             wait_and_barrier<6>();
         else
             wait_and_barrier<0>();
-        if (g + S - 1 < g1)
-            issue_stage<SH, KIND>(T, g + S - 1, smem + ((it + S - 1) % S) * Lds<SH>::STAGE, wave, lane);
-        const uint8_t* stage = smem + (it % S) * Lds<SH>::STAGE;
+        if (g + S - 1 < g1) stg.issue(T, g + S - 1, smem, ((SS + S - 1) % S) * Lds<SH>::STAGE, wave);
+        const uint8_t* stage = smem + SS * Lds<SH>::STAGE;
         if constexpr (ACC == 0 && KIND == 0) {
             if (wm * 64 < m_valid) compute_f32_block<SH>(stage, wm, wn, lane, acc, pp, cp);
         } else if constexpr (ACC == 0) {
@@ -563,6 +596,11 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         } else {
             compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
         }
+    };
+    for (int64_t g = g0; g < g1; g += S) {
+        step(std::integral_constant<int, 0>(), g);
+        if (g + 1 < g1) step(std::integral_constant<int, 1>(), g + 1);
+        if (g + 2 < g1) step(std::integral_constant<int, 2>(), g + 2);
     }
     if constexpr (ACC == 0 && KIND == 0) {
 #pragma unroll
