@@ -67,6 +67,14 @@ struct Shape<0> {
     static constexpr int BM = 256, BN = 128;
     static constexpr int WGM = 4, WGN = 2;  // wave grid (m, n)
     static constexpr int STAGES = 3;
+    // Wave w runs on SIMD w % 4.  The two waves of a SIMD take one m-slot
+    // from the top half of the tile and one from the bottom half, so a tile
+    // with at most 128 valid rows (a typical expert) still keeps all four
+    // SIMDs' matrix cores busy.
+    __device__ static void wave_grid(int wave, int& wm, int& wn) {
+        wm = (wave & 1) + 2 * (wave >> 2);
+        wn = (wave >> 1) & 1;
+    }
 };
 
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
@@ -537,7 +545,8 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     constexpr int S = Shape<SH>::STAGES;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave % Shape<SH>::WGM, wn = wave / Shape<SH>::WGM;
+    int wm, wn;
+    Shape<SH>::wave_grid(wave, wm, wn);
     const int m_valid = (int)(T.m_end - T.m0 < Shape<SH>::BM ? T.m_end - T.m0 : Shape<SH>::BM);
 
     typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;
