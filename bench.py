@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum fp32|mfma8]
     python bench.py --traffic-probe     # plain copy of known size, for counter scaling
     python bench.py --workload expert_backward|grouped_upproj|decode_grouped
+    python bench.py --library-ceiling   # vendor GEMMs on the dense shape, for context
 
 The default line (--workload dense_fprop) is the headline measurement.  The
 other workloads print one JSON line of the same form for the other shapes
@@ -129,6 +130,42 @@ def cpu_baseline(X, W, target_s=20.0):
                       f"(quant 1x128 + quant 128x128 + GEMM {ms}x{ns}x{K}), {dt:.1f} s"}
 
 
+def library_ceiling():
+    """Time the vendor library (hipBLASLt through torch) on the dense Fprop
+    shape with random data: plain f16 and bf16 GEMMs and the per-tensor-scaled
+    FP8 GEMM.  None of them does block scaling or per-128 promotion; they are
+    the practical ceilings of the matrix cores on this shape and data."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        a = torch.randn(M, K, device=dev, generator=g).to(dt)
+        b = torch.randn(N, K, device=dev, generator=g).to(dt)
+        ms = timed(lambda: a @ b.t())
+        out[f"matmul_{name}"] = {"ms": ms, "TFLOP/s": 2.0 * M * N * K / ms / 1e9}
+        del a, b
+    a = torch.randn(M, K, device=dev, generator=g).to(torch.float8_e4m3fn)
+    b = torch.randn(N, K, device=dev, generator=g).to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    ms = timed(lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+    out["scaled_mm_fp8_per_tensor"] = {"ms": ms, "TFLOP/s": 2.0 * M * N * K / ms / 1e9}
+    print(json.dumps({"library_ceiling": out, "shape": [M, N, K], "data": "torch.randn"}), flush=True)
+
+
 PEAK_UNIT = {"TFLOP/s": (PEAK_FP8_TFLOPS, "mfma"), "GB/s": (PEAK_HBM_GBPS, "hbm")}
 
 
@@ -252,6 +289,8 @@ def main():
                     help="GEMM accumulation: exact group partials (fp32) or FP8 matrix cores (mfma8)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only a plain copy of known size (counter scaling)")
+    ap.add_argument("--library-ceiling", action="store_true",
+                    help="time the vendor GEMMs on the dense shape (context only)")
     ap.add_argument("--workload", default="dense_fprop",
                     choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped"])
     args = ap.parse_args()
@@ -262,6 +301,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.library_ceiling:
+        library_ceiling()
         return
     if args.workload != "dense_fprop":
         other_workload(args.workload, args)

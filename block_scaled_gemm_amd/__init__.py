@@ -30,7 +30,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 SCALE_FP32, SCALE_POW2 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 BSCALE_BLOCK, BSCALE_TILE = 0, 1
-ACCUM_FP32, ACCUM_MFMA8 = 0, 1
+ACCUM_FP32, ACCUM_MFMA8, ACCUM_MFMA8_POW2 = 0, 1, 2
 
 _lib = None
 

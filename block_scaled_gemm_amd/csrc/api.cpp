@@ -171,7 +171,8 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
                                       int64_t ldd, int out_dtype, int accum, void* workspace,
                                       size_t workspace_bytes, void* stream) {
     if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
-    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
+        return FP8BS_ERR_ARG;
     if (int r = check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
     if (M == 0 || N == 0) return FP8BS_OK;
     const size_t need = fp8_gemm_workspace_bytes(M, N, K);
@@ -207,7 +208,8 @@ FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t 
                                   const float* sb, void* d, int64_t ldd, int out_dtype, int accum,
                                   void* stream) {
     if (G < 0 || rows_bound < 0) return FP8BS_ERR_ARG;
-    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
+        return FP8BS_ERR_ARG;
     if (G > 0 && !offsets) return FP8BS_ERR_ARG;
     if (N % 128 != 0) return FP8BS_ERR_SHAPE;
     if (int r = check_gemm_common(rows_bound, N, K, a, lda, sa, ldsa, b, K, sb, d, ldd, out_dtype)) return r;

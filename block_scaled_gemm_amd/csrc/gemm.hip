@@ -6,7 +6,7 @@
 // (the per-group dequantisation rides on that FMA), as the pages' promotion
 // every 128 elements does.
 //
-// Two ways of forming P_g (the `accum` argument):
+// Three ways of forming P_g (the `accum` argument):
 //
 //  ACC_F32 (0, default).  The gfx950 FP8 matrix cores do not add their
 //  products at FP32 accuracy: on crafted inputs every FP8 MFMA form loses
@@ -23,7 +23,11 @@
 //  the matrix core's own limited accumulation inside the group.  Workgroup
 //  tile 256 (m) x 128 (n); 8 waves of 64x64, 4x4 sub-tiles of 16x16.
 //
-// Both: the MFMA's first operand is the B (weight) tile and its second the
+//  ACC_MFMA8_POW2 (2).  As ACC_MFMA8, for power-of-two scales: they enter
+//  the scaled MFMA as E8M0 block scales and every group is accumulated by
+//  the matrix core itself, so there is no promotion step on the VALU.
+//
+// All: the MFMA's first operand is the B (weight) tile and its second the
 // A (activation) tile, so each result sub-tile is D^T and every lane ends
 // with runs of four consecutive output columns of one row (one 8-byte bf16
 // or 16-byte fp32 store) and needs one activation scale per sub-tile.  Each
@@ -475,6 +479,47 @@ __device__ __forceinline__ void compute_mfma8(const uint8_t* stage, const Tile& 
     }
 }
 
+// ==== ACC_MFMA8_POW2 path: power-of-two scales inside the FP8 matrix cores ====================
+//
+// With every scale a power of two, 2^k is the E8M0 byte k + 127 -- the
+// exponent field of the fp32 scale.  The scaled MFMA multiplies lane l's
+// 32-element K block of its row by 2^(byte - 127) for each operand, so the
+// whole dequantised group dec(a)*sa * dec(b)*SB is summed by the matrix
+// core straight into the fp32 accumulator: no promotion on the VALU.  The
+// scale bytes are per (row, K block); a 128-element group's four blocks of a
+// row share its 1x128 or 128x128 scale.
+__device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+
+template <int SH, int KIND>
+__device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
+                                                   v4f (&acc)[4][4]) {
+    const uint8_t* la = stage + Lds<SH>::A;
+    const uint8_t* lb = stage + Lds<SH>::B;
+    const float* lsa = (const float*)(stage + Lds<SH>::SA);
+    const float* lsb = (const float*)(stage + Lds<SH>::SB);
+    const int mbase = wm * 64, nbase = wn * 64;
+    const int c0 = 2 * (lane >> 4);
+    if (mbase >= m_valid) return;
+
+    v8i bf[4];
+    int sbb[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        bf[j] = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+        sbb[j] = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (mbase + 16 * i >= m_valid) break;  // wave-uniform
+        const int mrow = mbase + 16 * i + (lane & 15);
+        const v8i af = f8_frag(la, mrow, c0);
+        const int sab = e8m0(lsa[mrow]);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbb[j], 0, sab);
+    }
+}
+
 // ==== epilogue ===========================================================================
 
 // Store four consecutive columns n..n+3 of row m (masked at the edges).
@@ -549,7 +594,7 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     Shape<SH>::wave_grid(wave, wm, wn);
     const int m_valid = (int)(T.m_end - T.m0 < Shape<SH>::BM ? T.m_end - T.m0 : Shape<SH>::BM);
 
-    typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;
+    typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;  // ACC 1, 2: 16x16 sub-tiles
     AccT acc;
     if constexpr (ACC == 0) {
 #pragma unroll
@@ -603,7 +648,10 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         } else if constexpr (ACC == 0) {
             compute_f32<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
         } else {
-            compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+            if constexpr (ACC == 1)
+                compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+            else
+                compute_mfma8_pow2<SH, KIND>(stage, wm, wn, lane, m_valid, acc);
         }
     };
     for (int64_t g = g0; g < g1; g += S) {
@@ -774,7 +822,8 @@ static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    return g.accum == 0 ? launch_gemm_acc<0>(g, st) : launch_gemm_acc<1>(g, st);
+    if (g.accum == 0) return launch_gemm_acc<0>(g, st);
+    return g.accum == 1 ? launch_gemm_acc<1>(g, st) : launch_gemm_acc<2>(g, st);
 }
 
 template <int ACC>
@@ -790,7 +839,8 @@ static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.G == 0 || g.N == 0) return hipSuccess;
-    return g.accum == 0 ? launch_grouped_acc<0>(g, st) : launch_grouped_acc<1>(g, st);
+    if (g.accum == 0) return launch_grouped_acc<0>(g, st);
+    return g.accum == 1 ? launch_grouped_acc<1>(g, st) : launch_grouped_acc<2>(g, st);
 }
 
 }  // namespace fp8bs

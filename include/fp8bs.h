@@ -92,8 +92,16 @@ enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_F32 = 1 };
  *    2^-12 of the largest product in the instruction -- the same limited
  *    accumulation the pages report for their tensor cores.  Contract:
  *    |D - exact| <= 2^-10 * sum_g |sa*SB| * sum_k |dec(a)*dec(b)|, plus the
- *    output rounding. */
-enum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_MFMA8 = 1 };
+ *    output rounding.
+ *  FP8BS_ACCUM_MFMA8_POW2: for power-of-two scales only (both operands
+ *    quantised with FP8BS_SCALE_POW2): the scales enter the FP8 matrix cores
+ *    as E8M0 block scales and each group is summed straight into the FP32
+ *    accumulator, with no promotion step -- the block-scaled
+ *    microscaling form of the method ([cameseeing-1171527], passage relating
+ *    the fine-grained scaling to microscaling formats).  Scales that are not
+ *    powers of two give wrong results; the error contract is that of
+ *    FP8BS_ACCUM_MFMA8. */
+enum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_MFMA8 = 1, FP8BS_ACCUM_MFMA8_POW2 = 2 };
 
 /* How the B operand's scales are addressed (SB(n, g) for column n of the
  * output and K group g). */
@@ -242,7 +250,7 @@ int fp8_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
  *          Dgrad (B = qt of W, its scales transposed): BLOCK, s0 = 1, s1 = lds.
  *          Wgrad (B from fp8_quant_tile COL):          TILE,  s0 = lds.
  *   d      output [M][ldd], bf16 bits (FP8BS_OUT_BF16) or fp32 (FP8BS_OUT_F32).
- *   accum  FP8BS_ACCUM_FP32 or FP8BS_ACCUM_MFMA8.
+ *   accum  FP8BS_ACCUM_FP32, FP8BS_ACCUM_MFMA8 or FP8BS_ACCUM_MFMA8_POW2.
  *   workspace  device scratch of at least fp8_gemm_workspace_bytes(M, N, K)
  *          bytes (may be NULL when that is 0); it holds split-K partials
  *          when K is long and the output small.  The reduction over splits
@@ -284,7 +292,7 @@ size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *            (fp8_quant_tile ROW of the rows gathered per expert).
  *   b        codes [G][N][K] (contiguous), sb  block scales [G][N/128][K/128].
  *   d        output [rows][ldd], bf16 or fp32 as out_dtype.
- *   accum    FP8BS_ACCUM_FP32 or FP8BS_ACCUM_MFMA8, as for the dense GEMM.
+ *   accum    one of FP8BS_ACCUM_*, as for the dense GEMM.
  * N and K must be multiples of 128.  Alignment as fp8_gemm_blockscaled;
  * ldsa >= rows_bound.
  * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.

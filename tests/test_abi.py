@@ -133,7 +133,7 @@ def _gemm(**kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(acc=2), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
+    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(acc=3), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
     (dict(M=-1), ARG), (dict(lda=256), ARG), (dict(ldd=128), ARG), (dict(ldsa=100), ARG),
     (dict(K=500, lda=512, ldb=512), SHAPE), (dict(a=FAKE + 8), ALIGN), (dict(d=FAKE + 4), ALIGN),
     (dict(lda=520), ALIGN), (dict(ldd=258), ALIGN), (dict(sa=FAKE + 1), ALIGN),

@@ -9,6 +9,7 @@ from gpu_util import workload, bf16_f64, dev, dev_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 ACCUMS = pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
+ACCUMS_POW2 = pytest.mark.parametrize("accum", [0, 1, 2], ids=["acc32", "mfma8", "mfma8pow2"])
 
 
 def check(y, r, rabs, out, accum, groups, tag):
@@ -44,7 +45,7 @@ def quant_experts(hip, orc, Xcat, W, mode):
             wqx, wsx, wqw.reshape(G, N, K), wsw.reshape(G, N // 128, K // 128))
 
 
-@ACCUMS
+@ACCUMS_POW2
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
 def test_grouped_small_with_empty_experts(hip, orc, out, accum):
     """6 experts with 0, 1, 130, 0, 257 and 40 rows (empty experts, a single
@@ -94,7 +95,7 @@ def _check_sampled(hip, orc, data, mode, tag, accum):
     check(out_f64(y)[mi, ni], r, rabs, 0, accum, wqw.shape[2] // 128, f"{tag} accum={accum}")
 
 
-@ACCUMS
+@ACCUMS_POW2
 def test_grouped_upproj_full_size(hip, orc, accum):
     """Workload 3: 32 local experts of a top-8-of-256 routing of 4096
     tokens, N = 4096, K = 7168, power-of-two scales, bf16 out."""
