@@ -14,6 +14,7 @@ Functions carry the C names (see include/fp8bs.h for the full contract):
     fp8_requant_col(q, s, scale_mode)               -> (qt, st)
     fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype) -> d
     fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype, rows_bound=None)    -> d
+    fp8_grouped_gemm_strided(offsets, a, sa, G, N, b, ldb, b_estride, sb, ...) -> d
 
 bf16 inputs are ``torch.bfloat16`` tensors (their bit patterns are what the
 library reads); codes are ``torch.uint8``; scales ``torch.float32``.
@@ -73,6 +74,9 @@ def lib():
         L.fp8_grouped_gemm.restype = i32
         L.fp8_grouped_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp, vp,
                                        i64, i32, i32, vp]
+        L.fp8_grouped_gemm_strided.restype = i32
+        L.fp8_grouped_gemm_strided.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, i64, i64, vp, i32,
+                                               i64, i64, i64, vp, i64, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -245,6 +249,39 @@ def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None,
                                   _ptr(b), _ptr(sb), _ptr(d), _ld(d), int(out_dtype), int(accum), _stream()),
            "fp8_grouped_gemm")
     return d
+
+
+def fp8_grouped_gemm_strided(offsets, a, sa, G, N, b, ldb, b_estride, sb, bscale_kind, sb_s0, sb_s1, sb_estride,
+                             out_dtype=OUT_BF16, rows_bound=None, d=None, accum=ACCUM_FP32):
+    """Grouped GEMM with strided per-expert B codes and scales (see
+    include/fp8bs.h): rows offsets[e]..offsets[e+1]-1 of a use codes at
+    b + e*b_estride (rows ldb apart) and scales at sb + e*sb_estride.  b and
+    sb are flat device tensors holding every expert."""
+    _dev(offsets, "offsets", torch.int32)
+    _dev(a, "a", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(b, "b", torch.uint8)
+    _dev(sb, "sb", torch.float32)
+    K = a.shape[1]
+    rows = a.shape[0] if rows_bound is None else int(rows_bound)
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if d is None:
+        d = torch.empty((rows, N), dtype=dt, device=a.device)
+    _check(lib().fp8_grouped_gemm_strided(int(G), rows, int(N), K, _ptr(offsets), _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                                          _ptr(b), int(ldb), int(b_estride), _ptr(sb), int(bscale_kind), int(sb_s0),
+                                          int(sb_s1), int(sb_estride), _ptr(d), _ld(d), int(out_dtype), int(accum),
+                                          _stream()), "fp8_grouped_gemm_strided")
+    return d
+
+
+def moe_dgrad(offsets, qdy, sdy, qwt, sw, G, out_dtype=OUT_F32, accum=ACCUM_FP32):
+    """M-grouped Dgrad of G experts: dX_e = dY_e W_e.  qdy, sdy: the 1x128
+    quantisation of the expert-sorted dY [rows, N_w]; qwt, sw: the transposed
+    codes [K_w, >=G*N_w] and scales [G*N_w/128, K_w/128] of the stacked
+    weights [G*N_w, K_w] from fp8_quant_block(transpose=True)."""
+    Kw, Nw = qwt.shape[0], qdy.shape[1]
+    return fp8_grouped_gemm_strided(offsets, qdy, sdy, G, Kw, qwt, _ld(qwt), Nw, sw, BSCALE_BLOCK, 1, _ld(sw),
+                                    (Nw // 128) * _ld(sw), out_dtype, accum=accum)
 
 
 # ---- the three GEMMs of a Linear ---------------------------------------------------

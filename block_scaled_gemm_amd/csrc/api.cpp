@@ -236,6 +236,48 @@ FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t 
     g.offsets = offsets;
     g.G = G;
     g.b_estride = N * K;
+    g.sb_s0 = K / 128;
+    g.sb_s1 = 1;
     g.sb_estride = (N / 128) * (K / 128);
+    return hip_status(fp8bs::launch_grouped_gemm(g, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_grouped_gemm_strided(int G, int64_t rows_bound, int64_t N, int64_t K, const int32_t* offsets,
+                                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                          const uint8_t* b, int64_t ldb, int64_t b_estride, const float* sb,
+                                          int bscale_kind, int64_t sb_s0, int64_t sb_s1, int64_t sb_estride,
+                                          void* d, int64_t ldd, int out_dtype, int accum, void* stream) {
+    if (G < 0 || rows_bound < 0 || b_estride < 0 || sb_estride < 0) return FP8BS_ERR_ARG;
+    if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
+        return FP8BS_ERR_ARG;
+    if (G > 0 && !offsets) return FP8BS_ERR_ARG;
+    if (int r = check_gemm_common(rows_bound, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
+    if (!aligned(offsets, 4) || (K > 0 && b_estride % 16 != 0)) return FP8BS_ERR_ALIGN;
+    if (G == 0 || N == 0 || rows_bound == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    fp8bs::GemmArgs g{};
+    g.M = rows_bound;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+    g.b = b;
+    g.ldb = ldb;
+    g.sb = sb;
+    g.bscale_kind = bscale_kind;
+    g.sb_s0 = sb_s0;
+    g.sb_s1 = sb_s1;
+    g.d = d;
+    g.ldd = ldd;
+    g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.accum = accum;
+    g.splits = 1;
+    g.offsets = offsets;
+    g.G = G;
+    g.b_estride = b_estride;
+    g.sb_estride = sb_estride;
     return hip_status(fp8bs::launch_grouped_gemm(g, (hipStream_t)stream));
 }

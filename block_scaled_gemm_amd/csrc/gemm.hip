@@ -711,7 +711,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
 }
 
 // Grouped: workgroup (expert e, n-tile) walks the expert's m-tiles.
-template <int ACC, int OUT_F32>
+template <int ACC, int KIND, int OUT_F32>
 __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -728,13 +728,13 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     T.sa = p.sa;
     T.ldsa = p.ldsa;
     T.b = p.b + e * p.b_estride;
-    T.ldb = p.K;
+    T.ldb = p.ldb;
     T.sb = p.sb + e * p.sb_estride;
-    T.sb_s0 = p.K / 128;
-    T.sb_s1 = 1;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = p.sb_s1;
     for (int64_t m0 = r0; m0 < r1; m0 += Shape<0>::BM) {
         T.m0 = m0;
-        run_tile<ACC, 0, 0, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
+        run_tile<ACC, 0, KIND, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
     }
 }
 
@@ -830,10 +830,17 @@ template <int ACC>
 static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     const dim3 grid((unsigned)(tiles_n * g.G));
-    if (g.out_f32)
-        hipLaunchKernelGGL((grouped_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
-    else
-        hipLaunchKernelGGL((grouped_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+    if (g.bscale_kind == 0) {
+        if (g.out_f32)
+            hipLaunchKernelGGL((grouped_kernel<ACC, 0, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        else
+            hipLaunchKernelGGL((grouped_kernel<ACC, 0, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+    } else {
+        if (g.out_f32)
+            hipLaunchKernelGGL((grouped_kernel<ACC, 1, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        else
+            hipLaunchKernelGGL((grouped_kernel<ACC, 1, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+    }
     return hipGetLastError();
 }
 

@@ -28,7 +28,8 @@ hipError_t launch_requant_col(const uint8_t* q, int64_t rows, int64_t cols, int6
 
 // Everything a block-scaled GEMM launch needs.  For a grouped launch,
 // `offsets` is non-null, `G` experts share N and K, expert e's codes start at
-// b + e*b_estride and its block scales at sb + e*sb_estride.
+// b + e*b_estride (rows ldb apart) and its B scales at sb + e*sb_estride
+// (addressed through bscale_kind, sb_s0, sb_s1 as in a dense launch).
 struct GemmArgs {
     int64_t M, N, K;
     const uint8_t* a;

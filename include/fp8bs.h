@@ -303,6 +303,32 @@ int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K,
                      const float *sb, void *d, int64_t ldd, int out_dtype,
                      int accum, void *stream);
 
+/*
+ * fp8_grouped_gemm_strided -- fp8_grouped_gemm with the experts' B codes and
+ * scales addressed by strides, so the same call serves the MoE backward
+ * GEMMs that read the forward weights transposed (M-grouped Dgrad:
+ * dX_e = dY_e * W_e from the transposed copy of the stacked weight
+ * quantisation; all three GEMMs in FP8, [why-be-59061] Figure 6 passage):
+ *
+ *   D[m][n] = sum_g sa[g*ldsa + m] * SB_e(n, g) *
+ *             sum_{k in g} dec(a[m*lda + k]) * dec(b[e*b_estride + n*ldb + k])
+ *   SB_e(n, g) = sb[e*sb_estride + (n/128)*sb_s0 + g*sb_s1]   (BLOCK)
+ *              = sb[e*sb_estride + g*sb_s0 + n]              (TILE)
+ *
+ * for rows m of expert e (offsets[e] <= m < offsets[e+1]); other arguments
+ * as fp8_grouped_gemm.  K must be a multiple of 128 (N any); b_estride a
+ * multiple of 16; alignment otherwise as fp8_gemm_blockscaled.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_grouped_gemm_strided(int G, int64_t rows_bound, int64_t N, int64_t K,
+                             const int32_t *offsets, const uint8_t *a,
+                             int64_t lda, const float *sa, int64_t ldsa,
+                             const uint8_t *b, int64_t ldb, int64_t b_estride,
+                             const float *sb, int bscale_kind, int64_t sb_s0,
+                             int64_t sb_s1, int64_t sb_estride, void *d,
+                             int64_t ldd, int out_dtype, int accum,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
+              "fp8_grouped_gemm_strided",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -167,6 +168,24 @@ def _grouped(**kw):
 ])
 def test_grouped_validation(kw, want):
     assert _grouped(**kw) == want
+
+
+def _gstrided(**kw):
+    a = dict(G=4, rows=512, N=200, K=512, off=FAKE, a=FAKE, lda=512, sa=FAKE, ldsa=512, b=FAKE, ldb=512,
+             bes=512 * 256, sb=FAKE, kind=0, s0=4, s1=1, ses=8, d=FAKE, ldd=256, out=0, acc=0)
+    a.update(kw)
+    return bs.lib().fp8_grouped_gemm_strided(a["G"], a["rows"], a["N"], a["K"], a["off"], a["a"], a["lda"], a["sa"],
+                                             a["ldsa"], a["b"], a["ldb"], a["bes"], a["sb"], a["kind"], a["s0"],
+                                             a["s1"], a["ses"], a["d"], a["ldd"], a["out"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=-1), ARG), (dict(kind=2), ARG), (dict(acc=3), ARG), (dict(off=None), ARG), (dict(bes=-16), ARG),
+    (dict(ses=-1), ARG), (dict(ldb=256), ARG), (dict(K=500, lda=512, ldb=512), SHAPE), (dict(bes=520), ALIGN),
+    (dict(ldb=520), ALIGN), (dict(off=FAKE + 2), ALIGN), (dict(G=0), OK), (dict(N=0), OK),
+])
+def test_grouped_strided_validation(kw, want):
+    assert _gstrided(**kw) == want
 
 
 def test_cast_validation():

@@ -106,3 +106,57 @@ def test_grouped_upproj_full_size(hip, orc, accum):
 def test_decode_grouped_full_size(hip, orc, accum):
     """Workload 4a: 64 experts with 1..256 rows each, N = 2048, K = 7168."""
     _check_sampled(hip, orc, workload("decode_grouped"), 0, "decode grouped", accum)
+
+
+def _moe_dgrad_case(hip, orc, dY, W, offsets, accum, tag, sample=None):
+    """M-grouped Dgrad dX_e = dY_e W_e through the strided grouped GEMM,
+    reading the transposed copy of the stacked weight quantisation; the
+    oracle is the dense oracle GEMM per expert on the same codes."""
+    G, Nw, Kw = W.shape
+    qd, sd = hip.fp8_quant_tile(dev_bf16(dY), hip.AXIS_ROW, 0)
+    wqd, wsd = orc.quant_tile(dY, 0, 0)
+    np.testing.assert_array_equal(host(qd), wqd)
+    _, sw, qwt = hip.fp8_quant_block(dev_bf16(W.reshape(G * Nw, Kw)), 0, transpose=True)
+    _, wsw, wqwt = orc.quant_block(W.reshape(G * Nw, Kw), 0, transpose=True)
+    np.testing.assert_array_equal(host(qwt), wqwt)
+    dx = hip.moe_dgrad(dev(offsets), qd, sd, qwt, sw, G, out_dtype=1, accum=accum)
+    y = out_f64(dx)
+    for e in range(G):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        a, sa = wqd[r0:r1], np.ascontiguousarray(wsd[:, r0:r1])
+        b = np.ascontiguousarray(wqwt[:, e * Nw:(e + 1) * Nw])
+        sbe = np.ascontiguousarray(wsw[e * Nw // 128:(e + 1) * Nw // 128])
+        if sample is None:
+            r = orc.gemm(a, sa, b, sbe, 0, 1, sbe.shape[1])
+            rabs = orc.gemm(a & 0x7F, sa, b & 0x7F, sbe, 0, 1, sbe.shape[1])
+            got = y[r0:r1]
+        else:
+            rng = np.random.default_rng(e)
+            mi, ni = rng.integers(0, r1 - r0, sample), rng.integers(0, Kw, sample)
+            r = orc.gemm_entries(a, sa, b, sbe, 0, 1, sbe.shape[1], mi, ni)
+            rabs = orc.gemm_entries(a & 0x7F, sa, b & 0x7F, sbe, 0, 1, sbe.shape[1], mi, ni)
+            got = y[r0:r1][mi, ni]
+        check(got, r, rabs, 1, accum, Nw // 128, f"{tag} expert {e}")
+
+
+@ACCUMS
+def test_moe_dgrad_small(hip, orc, accum):
+    """6 experts with 0, 1, 130, 0, 257 and 40 rows, N_w = 256, K_w = 384
+    (ragged tiles, empty experts), fp32 out, every output compared."""
+    counts = [0, 1, 130, 0, 257, 40]
+    offsets = np.zeros(len(counts) + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    dY = inputs.random_bf16(211, (int(offsets[-1]), 256), sd=1e-3)
+    W = inputs.random_bf16(212, (len(counts), 256, 384), sd=0.02, outliers=False)
+    _moe_dgrad_case(hip, orc, dY, W, offsets, accum, f"moe dgrad small accum={accum}")
+
+
+def test_moe_dgrad_upproj_full_size(hip, orc):
+    """Dgrad of the grouped up-projection at its real size: 32 experts,
+    W_e[4096 x 7168], dY[rows x 4096] N(0,1e-3) with outliers, sampled."""
+    data = workload("grouped_upproj")
+    offsets = data["offsets"]
+    dY = inputs.random_bf16(213, (int(offsets[-1]), 4096), sd=1e-3)
+    _moe_dgrad_case(hip, orc, dY, data["W"], offsets, 0, "moe dgrad up-proj", sample=200)
