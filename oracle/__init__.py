@@ -56,6 +56,9 @@ def _declare(L):
     L.orc_quant_block.restype = ctypes.c_int
     L.orc_quant_block.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int,
                                   _u8p, _i64, _u8p, _i64, _f32p, _i64]
+    L.orc_quant_tile_grouped_col.restype = ctypes.c_int
+    L.orc_quant_tile_grouped_col.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int, _i32p, ctypes.c_int,
+                                             _u8p, _i64, _f32p, _i64, ctypes.POINTER(ctypes.c_int64)]
     L.orc_requant_col.restype = ctypes.c_int
     L.orc_requant_col.argtypes = [_u8p, _i64, _i64, _i64, _f32p, _i64,
                                   ctypes.c_int, _u8p, _i64, _f32p, _i64]
@@ -154,6 +157,25 @@ class Oracle:
                                       rows, _p(s, _f32p), s.shape[1]),
                "quant_block")
         return q, s, qt
+
+    def quant_tile_grouped_col(self, x, offsets, pow2):
+        """128x1 groups restarted at each expert boundary (see oracle.h).
+        x: bf16 bits [T, C]; offsets int32 [G+1].  Returns (q [C, Tpad],
+        s [Tpad/128, C])."""
+        x = _c(x, np.uint16)
+        offsets = _c(offsets, np.int32)
+        T, C = x.shape
+        G = offsets.size - 1
+        tpad = int(sum((int(offsets[e + 1] - offsets[e]) + 127) // 128 * 128 for e in range(G)))
+        q = np.empty((C, max(tpad, 1)), np.uint8)[:, :tpad]
+        q = np.ascontiguousarray(q)
+        s = np.empty((tpad // 128, C), np.float32)
+        tp = ctypes.c_int64(0)
+        _check(self.L.orc_quant_tile_grouped_col(_p(x, _u16p), T, C, C, G, _p(offsets, _i32p), int(pow2),
+                                                 _p(q, _u8p), max(tpad, 1), _p(s, _f32p), C, ctypes.byref(tp)),
+               "quant_tile_grouped_col")
+        assert tp.value == tpad
+        return q, s
 
     def requant_col(self, q, s, pow2):
         """Backward re-tiling: codes q[rows, cols] in 1x128 row groups with
@@ -285,6 +307,10 @@ def quant_block(w, pow2, transpose=False):
 
 def requant_col(q, s, pow2):
     return default().requant_col(q, s, pow2)
+
+
+def quant_tile_grouped_col(x, offsets, pow2):
+    return default().quant_tile_grouped_col(x, offsets, pow2)
 
 
 def gemm(a, sa, b, sb, bscale_kind, sb_s0, sb_s1):

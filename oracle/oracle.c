@@ -222,6 +222,53 @@ int orc_quant_tile(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
     return ORC_OK;
 }
 
+/* 128x1 groups restarted at every expert boundary (reading: the pages give
+ * the 128x1 tiles of the backward pass for one matrix; for tokens routed to
+ * experts a group must not mix two experts' tokens, so each expert's tokens
+ * are grouped from its first token and its last group may be partial).
+ * Transposed output on a padded token axis so that every expert starts on
+ * a 128-element boundary. */
+int orc_quant_tile_grouped_col(const uint16_t *x, int64_t T, int64_t C,
+                               int64_t ldx, int G, const int32_t *offsets,
+                               int pow2, uint8_t *q, int64_t ldq, float *s,
+                               int64_t lds, int64_t *tp)
+{
+    if (!x || !offsets || !q || !s || !tp || T < 0 || C < 0 || G < 0 ||
+        ldx < C || lds < C)
+        return ORC_ERR_ARG;
+    if (offsets[0] != 0 || offsets[G] > T)
+        return ORC_ERR_ARG;
+    int64_t pad = 0;
+    for (int e = 0; e < G; e++) {
+        int64_t n = (int64_t)offsets[e + 1] - offsets[e];
+        if (n < 0)
+            return ORC_ERR_ARG;
+        pad += (n + 127) / 128 * 128;
+    }
+    *tp = pad;
+    if (ldq < pad)
+        return ORC_ERR_ARG;
+    int64_t start = 0; /* padded position of the current expert */
+    for (int e = 0; e < G; e++) {
+        int64_t r0 = offsets[e], n = (int64_t)offsets[e + 1] - offsets[e];
+        int64_t ng = (n + 127) / 128;
+        int64_t c;
+#pragma omp parallel for schedule(static)
+        for (c = 0; c < C; c++) {
+            for (int64_t j = 0; j < ng; j++) {
+                int64_t len = n - j * 128 < 128 ? n - j * 128 : 128;
+                uint8_t *out = q + c * ldq + start + j * 128;
+                s[(start / 128 + j) * lds + c] =
+                    quantise_group(x + (r0 + j * 128) * ldx + c, ldx, len, pow2, out, 1);
+                for (int64_t i = len; i < 128; i++)
+                    out[i] = 0; /* padding */
+            }
+        }
+        start += ng * 128;
+    }
+    return ORC_OK;
+}
+
 int orc_quant_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ldw,
                     int pow2, uint8_t *q, int64_t ldq, uint8_t *qt,
                     int64_t ldqt, float *s, int64_t lds)

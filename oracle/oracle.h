@@ -74,6 +74,21 @@ int orc_quant_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ldw,
                     int pow2, uint8_t *q, int64_t ldq, uint8_t *qt,
                     int64_t ldqt, float *s, int64_t lds);
 
+/* 128x1 groups along the tokens of each expert.  x [T][ldx] holds the
+ * tokens of G experts back to back: expert e owns rows offsets[e] ..
+ * offsets[e+1]-1.  Each expert's tokens are cut into groups of 128 starting
+ * at its first token; the last group holds the n_e mod 128 remaining tokens
+ * (its amax is taken over those only).  Codes are written transposed into a
+ * padded token axis where expert e starts at P_e = 128 * sum_{e'<e}
+ * ceil(n_e'/128): q[c*ldq + P_e + i] for token offsets[e] + i, zero codes in
+ * the padding; the scale of padded group p of column c is s[p*lds + c]
+ * (padded groups of the padding tail of an expert do not exist: every
+ * padded group holds at least one token).  Returns the padded length in *tp. */
+int orc_quant_tile_grouped_col(const uint16_t *x, int64_t T, int64_t C,
+                               int64_t ldx, int G, const int32_t *offsets,
+                               int pow2, uint8_t *q, int64_t ldq, float *s,
+                               int64_t lds, int64_t *tp);
+
 /* ---- backward re-tiling ----------------------------------------------------
  * q [rows][ldq] holds codes quantised in 1x128 row groups with scales
  * s[g*lds + r] (the layout orc_quant_tile writes for axis 0).  The matrix is

@@ -340,6 +340,58 @@ def check_block_vs_rows(orc, seed=29):
         assert np.all(sr == sb[0][:, None])
 
 
+# ---- 128x1 groups per expert ---------------------------------------------------------
+
+def check_grouped_col_aligned(orc, seed=59):
+    """When every expert's token count is a multiple of 128 there is no
+    padding, and the per-expert grouping equals quant_tile(axis 1) of each
+    expert's rows, concatenated along the token axis."""
+    rng = np.random.default_rng(seed)
+    counts = [128, 0, 256, 128]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    f = (rng.standard_normal((int(offsets[-1]), 192)) * 10.0 ** rng.uniform(-3, 3, (int(offsets[-1]), 1))).astype(np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    for pow2 in (0, 1):
+        q, s = orc.quant_tile_grouped_col(bits, offsets, pow2)
+        assert q.shape == (192, 512) and s.shape == (4, 192)
+        for e in range(len(counts)):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 == r0:
+                continue
+            qe, se = orc.quant_tile(np.ascontiguousarray(bits[r0:r1]), 1, pow2)
+            np.testing.assert_array_equal(q[:, r0:r1], qe)
+            np.testing.assert_array_equal(s[r0 // 128:r1 // 128], se)
+
+
+def check_grouped_col_partial(orc, seed=61):
+    """Ragged experts (0, 1, 130, 0, 257, 40 tokens): every group, the
+    partial last ones included, matches the brute-force group quantiser on
+    exactly that expert's tokens, the padding holds zero codes, and each
+    expert starts on a 128-token boundary of the padded axis."""
+    rng = np.random.default_rng(seed)
+    table = orc.decode_table()
+    counts = [0, 1, 130, 0, 257, 40]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    f = (rng.standard_normal((int(offsets[-1]), 16)) * 3).astype(np.float32)
+    f[rng.random(f.shape) < 0.02] *= 100
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    for pow2 in (0, 1):
+        q, s = orc.quant_tile_grouped_col(bits, offsets, pow2)
+        assert q.shape == (16, 7 * 128) and s.shape == (7, 16)
+        start = 0
+        for e, n in enumerate(counts):
+            for j in range((n + 127) // 128):
+                length = min(128, n - 128 * j)
+                rows = int(offsets[e]) + 128 * j + np.arange(length)
+                for c in (0, 5, 15):
+                    want, ws = brute_group(bits[rows, c], pow2, table)
+                    got = q[c, start + 128 * j:start + 128 * j + 128]
+                    np.testing.assert_array_equal(got[:length], want, err_msg=f"pow2={pow2} e={e} j={j} c={c}")
+                    assert np.all(got[length:] == 0)
+                    assert s[start // 128 + j, c] == ws
+            start += (n + 127) // 128 * 128
+
+
 # ---- backward re-tiling ------------------------------------------------------------
 
 def check_requant_bruteforce(orc, seed=47):
@@ -534,4 +586,5 @@ ALL_CHECKS = [
     check_block_vs_rows, check_gemm_bruteforce, check_gemm_identity,
     check_gemm_integers, check_gemm_entries_and_grouped, check_scale_edges,
     check_requant_bruteforce, check_requant_exact_dequant, check_requant_fp32_dequant,
+    check_grouped_col_aligned, check_grouped_col_partial,
 ]

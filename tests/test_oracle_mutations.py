@@ -72,6 +72,15 @@ MUTATIONS = {
     "requant_not_transposed": (
         "qt[c * ldqt + g * 128 + i] = orc_e4m3_encode(x[i] * inv);",
         "qt[(g * 128 + i) * cols + c] = orc_e4m3_encode(x[i] * inv);"),
+    "grouped_col_padding_not_zero": (
+        "                    out[i] = 0; /* padding */",
+        "                    out[i] = 0x7E; /* padding */"),
+    "grouped_col_scale_slot_first_group": (
+        "s[(start / 128 + j) * lds + c] =",
+        "s[(start / 128) * lds + c] ="),
+    "grouped_col_unpadded_start": (
+        "        start += ng * 128;",
+        "        start += n;"),
     "b_reversed_within_group": (
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[k]];",
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[g * 128 + 127 - (k - g * 128)]];"),
