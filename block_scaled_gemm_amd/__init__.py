@@ -77,6 +77,13 @@ def lib():
         L.fp8_grouped_gemm_strided.restype = i32
         L.fp8_grouped_gemm_strided.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, i64, i64, vp, i32,
                                                i64, i64, i64, vp, i64, i32, i32, vp]
+        L.fp8_grouped_col_bound.restype = i64
+        L.fp8_grouped_col_bound.argtypes = [i64, i32]
+        L.fp8_quant_tile_grouped_col.restype = i32
+        L.fp8_quant_tile_grouped_col.argtypes = [vp, i64, i64, i64, i32, vp, i32, vp, i64, vp, i64, vp]
+        L.fp8_grouped_gemm_kgrouped.restype = i32
+        L.fp8_grouped_gemm_kgrouped.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64, vp,
+                                                i64, i64, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -176,6 +183,27 @@ def fp8_quant_dual(x, scale_mode=SCALE_FP32):
     _check(lib().fp8_quant_dual(_ptr(x), rows, cols, _ld(x), int(scale_mode), _ptr(qr), _ld(qr), _ptr(sr),
                                 _ld(sr), _ptr(qc), _ld(qc), _ptr(sc), _ld(sc), _stream()), "fp8_quant_dual")
     return qr, sr, qc, sc
+
+
+def grouped_col_bound(T, G):
+    return int(lib().fp8_grouped_col_bound(int(T), int(G)))
+
+
+def fp8_quant_tile_grouped_col(x, offsets, scale_mode=SCALE_FP32):
+    """128x1 groups restarted at every expert boundary of the expert-sorted
+    tokens x [T, cols] (offsets: int32 device [G+1]).  Returns q [cols, Kb]
+    and s [Kb/128, cols] on the padded token axis, Kb = grouped_col_bound(T, G)
+    (bytes past the experts' last group are left as allocated)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(offsets, "offsets", torch.int32)
+    T, cols = x.shape
+    G = offsets.numel() - 1
+    kb = grouped_col_bound(T, G)
+    q = torch.zeros((cols, kb), dtype=torch.uint8, device=x.device)
+    s = torch.ones((kb // 128, cols), dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quant_tile_grouped_col(_ptr(x), T, cols, _ld(x), G, _ptr(offsets), int(scale_mode), _ptr(q),
+                                            _ld(q), _ptr(s), _ld(s), _stream()), "fp8_quant_tile_grouped_col")
+    return q, s
 
 
 def fp8_requant_col(q, s, scale_mode=SCALE_FP32, qt=None, st=None):
@@ -282,6 +310,36 @@ def moe_dgrad(offsets, qdy, sdy, qwt, sw, G, out_dtype=OUT_F32, accum=ACCUM_FP32
     Kw, Nw = qwt.shape[0], qdy.shape[1]
     return fp8_grouped_gemm_strided(offsets, qdy, sdy, G, Kw, qwt, _ld(qwt), Nw, sw, BSCALE_BLOCK, 1, _ld(sw),
                                     (Nw // 128) * _ld(sw), out_dtype, accum=accum)
+
+
+def fp8_grouped_gemm_kgrouped(offsets, a, sa, b, sb, out_dtype=OUT_F32, d=None, accum=ACCUM_FP32):
+    """K-grouped expert GEMM: D[e] = sum over expert e's padded token groups
+    (see include/fp8bs.h).  a [M, K], sa [K/128, M], b [N, K], sb [K/128, N]
+    on the padded token axis; returns d [G, M, N]."""
+    _dev(offsets, "offsets", torch.int32)
+    _dev(a, "a", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(b, "b", torch.uint8)
+    _dev(sb, "sb", torch.float32)
+    G = offsets.numel() - 1
+    M, K = a.shape
+    N = b.shape[0]
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if d is None:
+        d = torch.empty((G, M, N), dtype=dt, device=a.device)
+    _check(lib().fp8_grouped_gemm_kgrouped(G, M, N, K, _ptr(offsets), _ptr(a), _ld(a), _ptr(sa), _ld(sa), _ptr(b),
+                                           _ld(b), _ptr(sb), _ld(sb), _ptr(d), d.stride(1), d.stride(0),
+                                           int(out_dtype), int(accum), _stream()), "fp8_grouped_gemm_kgrouped")
+    return d
+
+
+def moe_wgrad(offsets, dy, x, scale_mode=SCALE_FP32, out_dtype=OUT_F32, accum=ACCUM_FP32):
+    """K-grouped Wgrad of G experts, dW_e = dY_e^T X_e, from the
+    expert-sorted bf16 dY [T, N] and X [T, C]: both quantised in 128x1 groups
+    per expert, then summed over each expert's tokens.  Returns [G, N, C]."""
+    qdy, sdy = fp8_quant_tile_grouped_col(dy, offsets, scale_mode)
+    qx, sx = fp8_quant_tile_grouped_col(x, offsets, scale_mode)
+    return fp8_grouped_gemm_kgrouped(offsets, qdy, sdy, qx, sx, out_dtype, accum=accum)
 
 
 # ---- the three GEMMs of a Linear ---------------------------------------------------

@@ -105,6 +105,27 @@ FP8BS_EXPORT int fp8_quant_block(const uint16_t* w, int64_t rows, int64_t cols, 
                                                 ldqt, s, lds, (hipStream_t)stream));
 }
 
+FP8BS_EXPORT int64_t fp8_grouped_col_bound(int64_t T, int G) {
+    if (T < 0 || G < 0) return 0;
+    return fp8bs::grouped_col_bound(T, G);
+}
+
+FP8BS_EXPORT int fp8_quant_tile_grouped_col(const uint16_t* x, int64_t T, int64_t cols, int64_t ldx, int G,
+                                            const int32_t* offsets, int scale_mode, uint8_t* q, int64_t ldq,
+                                            float* s, int64_t lds, void* stream) {
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (T < 0 || cols < 0 || G < 0) return FP8BS_ERR_ARG;
+    if (G > 0 && cols > 0 && (!x || !offsets || !q || !s)) return FP8BS_ERR_ARG;
+    if (ldx < cols || lds < cols || ldq < fp8bs::grouped_col_bound(T, G)) return FP8BS_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(offsets, 4) || ldx % 8 != 0 ||
+        ldq % 16 != 0)
+        return FP8BS_ERR_ALIGN;
+    if (G == 0 || cols == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_quant_grouped_col(x, T, cols, ldx, G, offsets, scale_mode == FP8BS_SCALE_POW2, q,
+                                                      ldq, s, lds, (hipStream_t)stream));
+}
+
 FP8BS_EXPORT int fp8_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int scale_mode,
                                 uint8_t* qr, int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc,
                                 float* sc, int64_t ldsc, void* stream) {
@@ -240,6 +261,45 @@ FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t 
     g.sb_s1 = 1;
     g.sb_estride = (N / 128) * (K / 128);
     return hip_status(fp8bs::launch_grouped_gemm(g, (hipStream_t)stream));
+}
+
+FP8BS_EXPORT int fp8_grouped_gemm_kgrouped(int G, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
+                                           const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                           const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb, void* d,
+                                           int64_t ldd, int64_t d_estride, int out_dtype, int accum,
+                                           void* stream) {
+    if (G < 0) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
+        return FP8BS_ERR_ARG;
+    if (G > 0 && !offsets) return FP8BS_ERR_ARG;
+    if (int r = check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
+    if (ldsb < N || d_estride < M * ldd) return FP8BS_ERR_ARG;
+    if (!aligned(offsets, 4) || d_estride % 4 != 0) return FP8BS_ERR_ALIGN;
+    if (G == 0 || M == 0 || N == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    fp8bs::GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+    g.b = b;
+    g.ldb = ldb;
+    g.sb = sb;
+    g.bscale_kind = FP8BS_BSCALE_TILE;
+    g.sb_s0 = ldsb;
+    g.sb_s1 = 0;
+    g.d = d;
+    g.ldd = ldd;
+    g.d_estride = d_estride;
+    g.out_f32 = out_dtype == FP8BS_OUT_F32;
+    g.accum = accum;
+    g.splits = 1;
+    g.offsets = offsets;
+    g.G = G;
+    return hip_status(fp8bs::launch_kgrouped_gemm(g, (hipStream_t)stream));
 }
 
 FP8BS_EXPORT int fp8_grouped_gemm_strided(int G, int64_t rows_bound, int64_t N, int64_t K, const int32_t* offsets,

@@ -738,6 +738,55 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     }
 }
 
+// K-grouped (MoE Wgrad over each expert's tokens): workgroup (expert e,
+// output tile) sums the expert's K groups, which sit consecutively on the
+// padded token axis starting at group sum_{e'<e} ceil(n_e'/128).  An expert
+// without tokens writes zeros.
+__device__ __forceinline__ int64_t expert_first_group(const int32_t* __restrict__ offsets, int64_t e) {
+    __shared__ int64_t wsum[WAVES];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int64_t acc = 0;
+    for (int64_t i = t; i < e; i += THREADS) acc += ((int64_t)offsets[i + 1] - offsets[i] + 127) / 128;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    if (lane == 0) wsum[wave] = acc;
+    __syncthreads();
+    int64_t total = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) total += wsum[w];
+    __syncthreads();
+    return total;
+}
+
+template <int ACC, int OUT_F32>
+__global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
+    const int64_t per = tiles_m * tiles_n;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t e = wid / per;
+    int64_t tm, tn;
+    tile_coords(wid % per, tiles_m, tiles_n, tm, tn);
+    const int64_t g0 = expert_first_group(p.offsets, e);
+    const int64_t g1 = g0 + ((int64_t)p.offsets[e + 1] - p.offsets[e] + 127) / 128;
+
+    Tile T;
+    T.m0 = tm * Shape<0>::BM;
+    T.m_end = p.M;
+    T.n0 = tn * Shape<0>::BN;
+    T.n_end = p.N;
+    T.a = p.a;
+    T.lda = p.lda;
+    T.sa = p.sa;
+    T.ldsa = p.ldsa;
+    T.b = p.b;
+    T.ldb = p.ldb;
+    T.sb = p.sb;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = 0;
+    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT_F32 ? 4 : 2);
+    run_tile<ACC, 0, 1, OUT_F32>(T, g0, g1, d, p.ldd, smem);
+}
+
 // Sum split-K partials in split order and convert.
 template <int OUT_F32>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
@@ -842,6 +891,24 @@ static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
             hipLaunchKernelGGL((grouped_kernel<ACC, 1, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
     }
     return hipGetLastError();
+}
+
+template <int ACC>
+static hipError_t launch_kgrouped_acc(const GemmArgs& g, hipStream_t st) {
+    const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
+    const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
+    const dim3 grid((unsigned)(tiles_m * tiles_n * g.G));
+    if (g.out_f32)
+        hipLaunchKernelGGL((kgrouped_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((kgrouped_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_kgrouped_gemm(const GemmArgs& g, hipStream_t st) {
+    if (g.G == 0 || g.M == 0 || g.N == 0) return hipSuccess;
+    if (g.accum == 0) return launch_kgrouped_acc<0>(g, st);
+    return g.accum == 1 ? launch_kgrouped_acc<1>(g, st) : launch_kgrouped_acc<2>(g, st);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {

@@ -18,6 +18,13 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int
                               uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
                               int64_t lds, hipStream_t st);
 
+// Padded token bound of the per-expert 128x1 grouping: 128 * (ceil(T/128) + G).
+inline int64_t grouped_col_bound(int64_t T, int G) { return 128 * ((T + 127) / 128 + G); }
+
+hipError_t launch_quant_grouped_col(const uint16_t* x, int64_t T, int64_t cols, int64_t ldx, int G,
+                                    const int32_t* offsets, bool pow2, uint8_t* q, int64_t ldq, float* s,
+                                    int64_t lds, hipStream_t st);
+
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool pow2, uint8_t* qr,
                              int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc, float* sc,
                              int64_t ldsc, hipStream_t st);
@@ -53,6 +60,7 @@ struct GemmArgs {
     const int32_t* offsets;
     int G;
     int64_t b_estride, sb_estride;
+    int64_t d_estride;  // K-grouped: expert e writes d + e*d_estride elements
 };
 
 // Split count the dense GEMM uses for this shape (1 = no split).
@@ -62,5 +70,8 @@ size_t gemm_workspace(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);
+// K-grouped: expert e sums the K groups of its tokens on the padded token
+// axis of the per-expert 128x1 grouping; B scales are per column (tile kind).
+hipError_t launch_kgrouped_gemm(const GemmArgs& g, hipStream_t st);
 
 }  // namespace fp8bs

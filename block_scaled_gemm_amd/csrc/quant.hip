@@ -125,18 +125,15 @@ __device__ __forceinline__ uint4 load_chunk_masked(const uint16_t* __restrict__ 
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One 128x1 group per column for 64 columns: source rows xr[i*ldx], i < nrows
+// (rows nrows..127 read as zero: they add nothing to the amax and encode to
+// zero codes), codes to qg[col*ldq + i], scale to sg[col].
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t ldx,
-                                                        uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ s, int64_t lds,
-                                                        int64_t col_tiles) {
-    __shared__ uint32_t tile[64 * 64];
+__device__ __forceinline__ void col_group_tile(const uint16_t* __restrict__ xr, int nrows, int64_t cols,
+                                               int64_t ldx, int64_t c0, uint8_t* __restrict__ qg, int64_t ldq,
+                                               float* __restrict__ sg, uint32_t* tile) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t g = blockIdx.x / col_tiles;
-    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
-
     {
         const int chunk = lane >> 3, p = lane & 7;
         const int64_t col = c0 + chunk * 8;
@@ -144,10 +141,10 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
         uint4 lo[2], hi[2];
 #pragma unroll
         for (int it = 0; it < 2; it++) {
-            const int64_t r = g * 128 + wave * 32 + it * 16 + 2 * p;
-            const uint16_t* src = x + r * ldx + col;
-            lo[it] = ok ? load_chunk_masked(src, col, cols) : make_uint4(0, 0, 0, 0);
-            hi[it] = ok ? load_chunk_masked(src + ldx, col, cols) : make_uint4(0, 0, 0, 0);
+            const int r = wave * 32 + it * 16 + 2 * p;
+            const uint16_t* src = xr + r * ldx + col;
+            lo[it] = ok && r < nrows ? load_chunk_masked(src, col, cols) : make_uint4(0, 0, 0, 0);
+            hi[it] = ok && r + 1 < nrows ? load_chunk_masked(src + ldx, col, cols) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int it = 0; it < 2; it++) {
@@ -173,10 +170,90 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
         const GroupScale gs = group_scale(am, POW2);
         const int64_t col = c0 + c;
         if (col < cols) {
-            st_stream8(q + col * ldq + g * 128 + 8 * l, quant8(v, gs.inv));
-            if (l == 0) s[g * lds + col] = gs.s;
+            st_stream8(qg + col * ldq + 8 * l, quant8(v, gs.inv));
+            if (l == 0) sg[col] = gs.s;
         }
     }
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ldx,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t lds,
+                                                        int64_t col_tiles) {
+    __shared__ uint32_t tile[64 * 64];
+    const int64_t g = blockIdx.x / col_tiles;
+    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
+    col_group_tile<POW2>(x + g * 128 * ldx, 128, cols, ldx, c0, q + g * 128, ldq, s + g * lds, tile);
+}
+
+// ---- 128x1 groups restarted at every expert boundary ------------------------------------------
+//
+// Tokens of G experts lie back to back (expert e: rows offsets[e] ..
+// offsets[e+1]-1).  Every expert is cut into 128-token groups from its first
+// token, the last one possibly partial, and the groups are numbered
+// consecutively on a padded token axis (expert e starts at 128 * the number of
+// groups before it).  Workgroup (padded group p, 64 columns) finds its
+// expert with a block-wide prefix sum of the experts' group counts, then
+// quantises like quant_col_kernel with the rows past the expert's end read
+// as zero -- its padding codes come out zero.
+
+// Expert owning padded group p and the group's index inside it; e = -1 when
+// p is past the last group.  Every thread gets the result.
+__device__ __forceinline__ void find_expert_group(const int32_t* __restrict__ offsets, int G, int64_t p, int& e_out,
+                                                  int64_t& j_out) {
+    __shared__ int64_t wsum[4];
+    __shared__ int s_e;
+    __shared__ int64_t s_j;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    if (t == 0) s_e = -1;
+    int64_t base = 0;
+    for (int e0 = 0; e0 < G; e0 += 256) {
+        const int e = e0 + t;
+        const int64_t cnt = e < G ? ((int64_t)offsets[e + 1] - offsets[e] + 127) / 128 : 0;
+        int64_t incl = cnt;  // inclusive scan within the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int64_t before = base;
+        for (int w = 0; w < wave; w++) before += wsum[w];
+        const int64_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        const int64_t first = before + incl - cnt;
+        if (cnt > 0 && p >= first && p < first + cnt) {
+            s_e = e;
+            s_j = p - first;
+        }
+        base += total;
+        __syncthreads();
+    }
+    __syncthreads();
+    e_out = s_e;
+    j_out = s_e >= 0 ? s_j : 0;
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_grouped_col_kernel(const uint16_t* __restrict__ x, int64_t cols,
+                                                                int64_t ldx, int G,
+                                                                const int32_t* __restrict__ offsets,
+                                                                uint8_t* __restrict__ q, int64_t ldq,
+                                                                float* __restrict__ s, int64_t lds,
+                                                                int64_t col_tiles) {
+    __shared__ uint32_t tile[64 * 64];
+    const int64_t p = blockIdx.x / col_tiles;
+    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
+    int e;
+    int64_t j;
+    find_expert_group(offsets, G, p, e, j);
+    if (e < 0) return;  // past the last group (the grid is sized for a bound)
+    const int64_t r0 = (int64_t)offsets[e] + 128 * j;
+    const int64_t left = (int64_t)offsets[e + 1] - r0;
+    const int nrows = left < 128 ? (int)left : 128;
+    col_group_tile<POW2>(x + r0 * ldx, nrows, cols, ldx, c0, q + p * 128, ldq, s + p * lds, tile);
 }
 
 // ---- 128x128 blocks ----------------------------------------------------------------------
@@ -467,6 +544,21 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
     else
         hipLaunchKernelGGL(quant_dual_kernel<false>, grid, dim3(256), 0, st, x, ldx, qr, ldqr, sr, ldsr, qc, ldqc, sc,
                            ldsc, ct);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_grouped_col(const uint16_t* x, int64_t T, int64_t cols, int64_t ldx, int G,
+                                    const int32_t* offsets, bool pow2, uint8_t* q, int64_t ldq, float* s,
+                                    int64_t lds, hipStream_t st) {
+    if (cols == 0 || G == 0) return hipSuccess;
+    const int64_t ct = (cols + 63) / 64, groups = (T + 127) / 128 + G;
+    const dim3 grid((unsigned)(ct * groups));
+    if (pow2)
+        hipLaunchKernelGGL(quant_grouped_col_kernel<true>, grid, dim3(256), 0, st, x, cols, ldx, G, offsets, q, ldq,
+                           s, lds, ct);
+    else
+        hipLaunchKernelGGL(quant_grouped_col_kernel<false>, grid, dim3(256), 0, st, x, cols, ldx, G, offsets, q, ldq,
+                           s, lds, ct);
     return hipGetLastError();
 }
 

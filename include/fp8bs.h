@@ -179,6 +179,39 @@ int fp8_quant_block(const uint16_t *w, int64_t rows, int64_t cols,
                     void *stream);
 
 /*
+ * fp8_quant_tile_grouped_col -- 128x1 groups along the tokens of each MoE
+ * expert, for the K-grouped expert Wgrad ([hacks-368261] 128x1 tiles of the
+ * backward pass; [why-be-59061] expert GEMMs in FP8).  Reading: a group
+ * never mixes two experts' tokens.
+ *
+ *   x        bf16 bits [T][ldx]: the tokens of G experts back to back,
+ *            expert e owning rows offsets[e] .. offsets[e+1]-1.
+ *   offsets  DEVICE int32 [G+1], offsets[0] = 0, non-decreasing,
+ *            offsets[G] <= T (read only on the device).
+ *   Each expert's tokens form groups of 128 from its first token, the last
+ *   group holding the n_e mod 128 remaining ones (its amax over those
+ *   only).  Groups are numbered on a padded token axis on which expert e
+ *   starts at P_e = 128 * sum_{e'<e} ceil(n_e'/128):
+ *   q        codes [cols][ldq], TRANSPOSED: q[c][P_e + i] encodes
+ *            x[offsets[e] + i][c]; the padding of each expert's last group
+ *            holds zero codes; bytes past the last group are not written.
+ *   s        s[p*lds + c] is the scale of padded group p of column c.
+ *   ldq must be >= fp8_grouped_col_bound(T, G) and s must hold
+ *   fp8_grouped_col_bound(T, G)/128 rows.
+ * Alignment: x, q 16-byte aligned; ldx a multiple of 8; ldq a multiple of
+ * 16; s 4-byte aligned.  ldx >= cols, lds >= cols.
+ * Errors: ERR_ARG, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_quant_tile_grouped_col(const uint16_t *x, int64_t T, int64_t cols,
+                               int64_t ldx, int G, const int32_t *offsets,
+                               int scale_mode, uint8_t *q, int64_t ldq,
+                               float *s, int64_t lds, void *stream);
+
+/* Padded token bound of fp8_quant_tile_grouped_col: 128 * (ceil(T/128) + G),
+ * which is >= 128 * sum_e ceil(n_e/128) for any split of T tokens. */
+int64_t fp8_grouped_col_bound(int64_t T, int G);
+
+/*
  * fp8_quant_dual -- both activation groupings from one read of x: the 1x128
  * groups (as fp8_quant_tile with FP8BS_AXIS_ROW) and the 128x1 groups (as
  * FP8BS_AXIS_COL), for a gradient that feeds both Dgrad and Wgrad
@@ -302,6 +335,33 @@ int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K,
                      const float *sa, int64_t ldsa, const uint8_t *b,
                      const float *sb, void *d, int64_t ldd, int out_dtype,
                      int accum, void *stream);
+
+/*
+ * fp8_grouped_gemm_kgrouped -- the K-grouped expert GEMM of the MoE
+ * backward pass: expert e's weight gradient sums over its own tokens,
+ *
+ *   D_e[m][n] = sum_{p = P_e/128}^{P_e/128 + ceil(n_e/128) - 1}
+ *               sa[p*ldsa + m] * sb[p*ldsb + n] *
+ *               sum_{k in p} dec(a[m*lda + k]) * dec(b[n*ldb + k])
+ *
+ * with a, sa and b, sb both from fp8_quant_tile_grouped_col (dY and X of the
+ * expert-sorted tokens; padded token axis, zero codes in the padding, so
+ * partial groups add nothing extra).  D_e is [M][ldd] at d + e*d_estride
+ * elements; an expert without tokens gets zeros.
+ *   offsets  the same DEVICE token offsets [G+1] the quantiser used.
+ *   K        the padded token bound the operands were laid out for
+ *            (a multiple of 128, >= 128 * sum_e ceil(n_e/128)).
+ * Alignment as fp8_gemm_blockscaled; lda, ldb >= K; ldsa >= M; ldsb >= N;
+ * d_estride >= M*ldd and a multiple of 4.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_grouped_gemm_kgrouped(int G, int64_t M, int64_t N, int64_t K,
+                              const int32_t *offsets, const uint8_t *a,
+                              int64_t lda, const float *sa, int64_t ldsa,
+                              const uint8_t *b, int64_t ldb, const float *sb,
+                              int64_t ldsb, void *d, int64_t ldd,
+                              int64_t d_estride, int out_dtype, int accum,
+                              void *stream);
 
 /*
  * fp8_grouped_gemm_strided -- fp8_grouped_gemm with the experts' B codes and

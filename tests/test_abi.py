@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
-              "fp8_grouped_gemm_strided",
+              "fp8_grouped_gemm_strided", "fp8_quant_tile_grouped_col", "fp8_grouped_gemm_kgrouped",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -186,6 +186,45 @@ def _gstrided(**kw):
 ])
 def test_grouped_strided_validation(kw, want):
     assert _gstrided(**kw) == want
+
+
+def _gcol(**kw):
+    a = dict(x=FAKE, T=300, C=256, ldx=256, G=3, off=FAKE, mode=0, q=FAKE, ldq=768, s=FAKE, lds=256)
+    a.update(kw)
+    return bs.lib().fp8_quant_tile_grouped_col(a["x"], a["T"], a["C"], a["ldx"], a["G"], a["off"], a["mode"],
+                                               a["q"], a["ldq"], a["s"], a["lds"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mode=2), ARG), (dict(T=-1), ARG), (dict(G=-1), ARG), (dict(off=None), ARG), (dict(q=None), ARG),
+    (dict(ldx=128), ARG), (dict(lds=100), ARG), (dict(ldq=640), ARG), (dict(x=FAKE + 8), ALIGN),
+    (dict(q=FAKE + 4), ALIGN), (dict(ldq=776), ALIGN), (dict(ldx=260), ALIGN), (dict(G=0), OK), (dict(C=0), OK),
+])
+def test_grouped_col_validation(kw, want):
+    assert _gcol(**kw) == want
+
+
+def test_grouped_col_bound():
+    assert bs.grouped_col_bound(300, 3) == 128 * (3 + 3)
+    assert bs.grouped_col_bound(0, 0) == 0
+
+
+def _kgrouped(**kw):
+    a = dict(G=3, M=256, N=200, K=768, off=FAKE, a=FAKE, lda=768, sa=FAKE, ldsa=256, b=FAKE, ldb=768, sb=FAKE,
+             ldsb=200, d=FAKE, ldd=200, des=256 * 200, out=1, acc=0)
+    a.update(kw)
+    return bs.lib().fp8_grouped_gemm_kgrouped(a["G"], a["M"], a["N"], a["K"], a["off"], a["a"], a["lda"], a["sa"],
+                                              a["ldsa"], a["b"], a["ldb"], a["sb"], a["ldsb"], a["d"], a["ldd"],
+                                              a["des"], a["out"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=-1), ARG), (dict(acc=3), ARG), (dict(out=2), ARG), (dict(off=None), ARG), (dict(ldsb=100), ARG),
+    (dict(des=100), ARG), (dict(lda=640), ARG), (dict(K=700, lda=768, ldb=768), SHAPE), (dict(des=256 * 200 + 2), ALIGN),
+    (dict(off=FAKE + 1), ALIGN), (dict(G=0), OK), (dict(M=0, des=0), OK),
+])
+def test_kgrouped_validation(kw, want):
+    assert _kgrouped(**kw) == want
 
 
 def test_cast_validation():

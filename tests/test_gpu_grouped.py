@@ -160,3 +160,74 @@ def test_moe_dgrad_upproj_full_size(hip, orc):
     offsets = data["offsets"]
     dY = inputs.random_bf16(213, (int(offsets[-1]), 4096), sd=1e-3)
     _moe_dgrad_case(hip, orc, dY, data["W"], offsets, 0, "moe dgrad up-proj", sample=200)
+
+
+def _padded(counts):
+    starts, p = [], 0
+    for n in counts:
+        starts.append(p)
+        p += (n + 127) // 128 * 128
+    return starts, p
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
+def test_quant_grouped_col_small(hip, orc, mode):
+    """128x1 groups per expert (0, 1, 130, 0, 257, 40 tokens; 200 columns,
+    a ragged column tile): codes, padding and scales bit-exact."""
+    counts = [0, 1, 130, 0, 257, 40]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = inputs.random_bf16(221, (int(offsets[-1]), 200))
+    q, s = hip.fp8_quant_tile_grouped_col(dev_bf16(x), dev(offsets), mode)
+    wq, ws = orc.quant_tile_grouped_col(x, offsets, mode)
+    tp = wq.shape[1]
+    np.testing.assert_array_equal(host(q)[:, :tp], wq)
+    np.testing.assert_array_equal(host(s)[:tp // 128], ws)
+
+
+def _moe_wgrad_check(hip, orc, dY, X, offsets, accum, tag, sample=None):
+    counts = np.diff(offsets)
+    dw = hip.moe_wgrad(dev(offsets), dev_bf16(dY), dev_bf16(X), 0, out_dtype=1, accum=accum)
+    wqd, wsd = orc.quant_tile_grouped_col(dY, offsets, 0)
+    wqx, wsx = orc.quant_tile_grouped_col(X, offsets, 0)
+    starts, _ = _padded(counts)
+    N, C = dY.shape[1], X.shape[1]
+    for e, n in enumerate(counts):
+        if n == 0:
+            assert torch.count_nonzero(dw[e]).item() == 0
+            continue
+        k0, k1 = starts[e], starts[e] + (int(n) + 127) // 128 * 128
+        a, sa = np.ascontiguousarray(wqd[:, k0:k1]), np.ascontiguousarray(wsd[k0 // 128:k1 // 128])
+        b, sb = np.ascontiguousarray(wqx[:, k0:k1]), np.ascontiguousarray(wsx[k0 // 128:k1 // 128])
+        if sample is None:
+            r = orc.gemm(a, sa, b, sb, 1, sb.shape[1], 0)
+            rabs = orc.gemm(a & 0x7F, sa, b & 0x7F, sb, 1, sb.shape[1], 0)
+            got = host(dw[e]).astype(np.float64)
+        else:
+            rng = np.random.default_rng(e)
+            mi, ni = rng.integers(0, N, sample), rng.integers(0, C, sample)
+            r = orc.gemm_entries(a, sa, b, sb, 1, sb.shape[1], 0, mi, ni)
+            rabs = orc.gemm_entries(a & 0x7F, sa, b & 0x7F, sb, 1, sb.shape[1], 0, mi, ni)
+            got = dw[e][torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy().astype(np.float64)
+        check(got, r, rabs, 1, accum, (k1 - k0) // 128, f"{tag} expert {e}")
+
+
+@ACCUMS
+def test_moe_wgrad_small(hip, orc, accum):
+    """K-grouped Wgrad dW_e = dY_e^T X_e over ragged experts (0, 1, 130, 0,
+    257, 40 tokens), N = 256, C = 200: every output compared; experts
+    without tokens give zeros."""
+    counts = [0, 1, 130, 0, 257, 40]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dY = inputs.random_bf16(222, (int(offsets[-1]), 256), sd=1e-3)
+    X = inputs.random_bf16(223, (int(offsets[-1]), 200))
+    _moe_wgrad_check(hip, orc, dY, X, offsets, accum, f"moe wgrad small accum={accum}")
+
+
+def test_moe_wgrad_upproj_full_size(hip, orc):
+    """Wgrad of the grouped up-projection experts at their real size: 32
+    experts, dY[rows x 4096], X[rows x 7168] gathered per route, dW_e
+    [4096 x 7168] fp32, sampled."""
+    data = workload("grouped_upproj")
+    offsets = data["offsets"]
+    dY = inputs.random_bf16(224, (int(offsets[-1]), 4096), sd=1e-3)
+    _moe_wgrad_check(hip, orc, dY, data["Xcat"], offsets, 0, "moe wgrad up-proj", sample=200)
