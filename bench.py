@@ -14,7 +14,11 @@ the path is measured on (no CPU baseline):
   grouped_upproj: 32 local experts of a top-8-of-256 routing of 4096 tokens,
     quant X 1x128 + quant W[32x4096x7168] 128x128 (power-of-two scales) +
     grouped GEMM, bf16 out;
-  decode_grouped: 64 experts with 1..256 rows, N = 2048, same steps.
+  decode_grouped: 64 experts with 1..256 rows, N = 2048, same steps;
+  moe_backward: the up-projection experts' backward pass: dY[rows x 4096]
+    quantised 1x128, M-grouped Dgrad dX_e = dY_e W_e on the transposed
+    forward weight codes, dY and X quantised in 128x1 groups per expert,
+    K-grouped Wgrad dW_e = dY_e^T X_e, fp32 out.
 
 Workload: the dense Fprop at real width -- X[4096 x 7168] bf16 ~N(0,1) with
 0.1% x100 outliers, W[18432 x 7168] bf16 ~N(0,0.02).  One step is the whole
@@ -231,6 +235,46 @@ def other_workload(name, args):
         flops = 4.0 * T * Kw * Nw
         config = {"workload": "expert backward: quant dY[8192x2048] 1x128 and 128x1 in one pass + re-tile "
                               "X[8192x7168] 1x128 -> 128x1 + Dgrad 8192x7168x2048 + Wgrad 2048x7168x8192 -> fp32"}
+    elif name == "moe_backward":
+        d = inputs.grouped_upproj()
+        G, Nw, Kw = d["W"].shape
+        offs_h = d["offsets"]
+        rows = int(offs_h[-1])
+        offsets = torch.from_numpy(offs_h).to(dev)
+        dY = to_bf16(inputs.random_bf16(213, (rows, Nw), sd=1e-3))
+        X = to_bf16(d["Xcat"])
+        _, sw, qwt = bs.fp8_quant_block(to_bf16(d["W"].reshape(G * Nw, Kw)), bs.SCALE_FP32, transpose=True)
+        kb = bs.grouped_col_bound(rows, G)
+        qd = torch.empty((rows, Nw), dtype=torch.uint8, device=dev)
+        sd = torch.empty((Nw // 128, rows), dtype=torch.float32, device=dev)
+        dx = torch.empty((rows, Kw), dtype=torch.float32, device=dev)
+        qdt = torch.zeros((Nw, kb), dtype=torch.uint8, device=dev)
+        sdt = torch.ones((kb // 128, Nw), dtype=torch.float32, device=dev)
+        qxt = torch.zeros((Kw, kb), dtype=torch.uint8, device=dev)
+        sxt = torch.ones((kb // 128, Kw), dtype=torch.float32, device=dev)
+        dw = torch.empty((G, Nw, Kw), dtype=torch.float32, device=dev)
+        L = bs.lib()
+        st = lambda: torch.cuda.current_stream().cuda_stream
+
+        def gcol(x, q, s_):
+            bs._check(L.fp8_quant_tile_grouped_col(x.data_ptr(), rows, x.shape[1], x.stride(0), G, offsets.data_ptr(),
+                                                   bs.SCALE_FP32, q.data_ptr(), q.stride(0), s_.data_ptr(),
+                                                   s_.stride(0), st()), "fp8_quant_tile_grouped_col")
+        colb = lambda c: rows * c * 3 + 2 * 4 * (kb // 128) * c  # bf16 in, codes out, scales
+        kernels = [
+            (f"quant_tile dY[{rows}x{Nw}]", lambda: bs.fp8_quant_tile(dY, bs.AXIS_ROW, bs.SCALE_FP32, q=qd, s=sd),
+             quant_bytes_row(rows, Nw), "GB/s"),
+            (f"moe dgrad G={G} rows={rows} {Kw}x{Nw}", lambda: bs.fp8_grouped_gemm_strided(
+                offsets, qd, sd, G, Kw, qwt, qwt.stride(0), Nw, sw, bs.BSCALE_BLOCK, 1, sw.stride(0),
+                (Nw // 128) * sw.stride(0), bs.OUT_F32, d=dx, accum=accum), 2.0 * rows * Kw * Nw / 1e3, "TFLOP/s"),
+            (f"quant_grouped_col dY[{rows}x{Nw}]", lambda: gcol(dY, qdt, sdt), colb(Nw), "GB/s"),
+            (f"quant_grouped_col X[{rows}x{Kw}]", lambda: gcol(X, qxt, sxt), colb(Kw), "GB/s"),
+            (f"moe wgrad K-grouped G={G} {Nw}x{Kw}", lambda: bs.fp8_grouped_gemm_kgrouped(
+                offsets, qdt, sdt, qxt, sxt, bs.OUT_F32, d=dw, accum=accum), 2.0 * rows * Nw * Kw / 1e3, "TFLOP/s"),
+        ]
+        flops = 4.0 * rows * Nw * Kw
+        config = {"workload": f"moe_backward: {G} up-projection experts, {rows} routed rows, W_e[{Nw}x{Kw}]: "
+                              f"quant dY 1x128 + M-grouped Dgrad + dY and X 128x1 per expert + K-grouped Wgrad -> fp32"}
     else:
         d = inputs.grouped_upproj() if name == "grouped_upproj" else inputs.decode_grouped()
         G, N, K = d["W"].shape
@@ -292,7 +336,7 @@ def main():
     ap.add_argument("--library-ceiling", action="store_true",
                     help="time the vendor GEMMs on the dense shape (context only)")
     ap.add_argument("--workload", default="dense_fprop",
-                    choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped"])
+                    choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped", "moe_backward"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "

@@ -547,39 +547,73 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
     }
 }
 
-template <int OUT_F32>
-__device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T, int wm, int wn, int lane,
-                                          void* d, int64_t ldd) {
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t m = T.m0 + wm * 64 + 32 * i + (lane & 31);
-        if (m >= T.m_end) continue;
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int64_t n = T.n0 + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
-                if (n >= T.n_end) continue;
-                store4<OUT_F32>(d, ldd, m, n, T.n_end, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                acc[i][j][4 * q + 3]);
-            }
+// The tile leaves through LDS: every wave writes its accumulators into a
+// row-major fp32 image of the tile (row stride BN + 4 floats, which spreads
+// consecutive rows over the banks), then each row of the tile is stored with
+// 32 lanes writing 16 contiguous bytes each (fp32) or 8 (bf16).  Written
+// straight from the MFMA layout, a store instruction would touch 32 rows with
+// 32 bytes each; through LDS it writes whole 512- or 256-byte row segments,
+// which matters where the output is large next to the work (fp32 gradients
+// summed over few tokens).  The stages are free: every wave has left the K
+// loop (wait_and_barrier<0>) before this runs.
+template <int SH>
+struct Epi {
+    static constexpr int LD = Shape<SH>::BN + 4;
+    static_assert(Shape<SH>::BM * LD * 4 <= Lds<SH>::BYTES, "the tile image fits in the stages");
+};
+
+template <int SH>
+__device__ __forceinline__ void put4(float* ep, int row, int col, float v0, float v1, float v2, float v3) {
+    *(float4*)&ep[row * Epi<SH>::LD + col] = make_float4(v0, v1, v2, v3);
+}
+
+template <int SH, int OUT_F32>
+__device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T, void* d, int64_t ldd) {
+    constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
+    constexpr int LPR = BN / 4;               // lanes per row
+    constexpr int RPI = THREADS / LPR;        // rows per pass
+    const int t = threadIdx.x;
+    const int col = (t % LPR) * 4;
+    const int64_t n = T.n0 + col;
+#pragma unroll 4
+    for (int r = t / LPR; r < BM; r += RPI) {
+        const int64_t m = T.m0 + r;
+        if (m >= T.m_end || n >= T.n_end) continue;
+        const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
+        store4<OUT_F32>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
     }
 }
 
-template <int OUT_F32>
+template <int SH, int OUT_F32>
+__device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T, int wm, int wn, int lane,
+                                          void* d, int64_t ldd, uint8_t* smem) {
+    float* ep = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                put4<SH>(ep, wm * 64 + 32 * i + (lane & 31), wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5),
+                         acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __syncthreads();
+    write_tile_image<SH, OUT_F32>(ep, T, d, ldd);
+    __syncthreads();  // the stages may be refilled by a following tile
+}
+
+template <int SH, int OUT_F32>
 __device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& T, int wm, int wn, int lane,
-                                            void* d, int64_t ldd) {
+                                            void* d, int64_t ldd, uint8_t* smem) {
+    float* ep = (float*)smem;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int64_t m = T.m0 + wm * 64 + 16 * i + (lane & 15);
-        if (m >= T.m_end) continue;
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t n = T.n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
-            if (n >= T.n_end) continue;
-            store4<OUT_F32>(d, ldd, m, n, T.n_end, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        }
-    }
+        for (int j = 0; j < 4; j++)
+            put4<SH>(ep, wm * 64 + 16 * i + (lane & 15), wn * 64 + 16 * j + 4 * (lane >> 4), acc[i][j][0],
+                     acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    __syncthreads();
+    write_tile_image<SH, OUT_F32>(ep, T, d, ldd);
+    __syncthreads();
 }
 
 // ==== one tile: pipelined K loop, then the store ==============================================
@@ -668,9 +702,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     wait_and_barrier<0>();  // the LDS stages may be reused by a following tile
 
     if constexpr (ACC == 0)
-        store_f32<OUT_F32>(acc, T, wm, wn, lane, d, ldd);
+        store_f32<SH, OUT_F32>(acc, T, wm, wn, lane, d, ldd, smem);
     else
-        store_mfma8<OUT_F32>(acc, T, wm, wn, lane, d, ldd);
+        store_mfma8<SH, OUT_F32>(acc, T, wm, wn, lane, d, ldd, smem);
 }
 
 // ==== kernels ==========================================================================
