@@ -84,6 +84,9 @@ def lib():
         L.fp8_grouped_gemm_kgrouped.restype = i32
         L.fp8_grouped_gemm_kgrouped.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                                 i64, i64, i32, i32, vp]
+        L.fp8_gemm_blockscaled_quant.restype = i32
+        L.fp8_gemm_blockscaled_quant.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32, i64, i64, i32,
+                                                 vp, i64, vp, i64, i32, vp]
         _lib = L
     return _lib
 
@@ -254,6 +257,28 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_
                                       _ptr(workspace) if workspace is not None else None, ws_bytes,
                                       _stream()), "fp8_gemm_blockscaled")
     return d
+
+
+def fp8_gemm_blockscaled_quant(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, scale_mode=SCALE_FP32, q=None, s=None,
+                               accum=ACCUM_FP32):
+    """The GEMM with its bf16 result quantised 1x128 along n in the
+    epilogue: returns (q [M, N] codes, s [N/128, M] scales), equal to
+    fp8_quant_tile(fp8_gemm_blockscaled(..., OUT_BF16), AXIS_ROW, scale_mode)."""
+    _dev(a, "a", torch.uint8)
+    _dev(b, "b", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(sb, "sb", torch.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    if s is None:
+        s = torch.empty((N // 128, M), dtype=torch.float32, device=a.device)
+    _check(lib().fp8_gemm_blockscaled_quant(M, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa), _ptr(b), _ld(b), _ptr(sb),
+                                            int(bscale_kind), int(sb_s0), int(sb_s1), int(scale_mode), _ptr(q),
+                                            _ld(q), _ptr(s), _ld(s), int(accum), _stream()),
+           "fp8_gemm_blockscaled_quant")
+    return q, s
 
 
 def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None, d=None,

@@ -224,6 +224,49 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
     return hip_status(fp8bs::launch_gemm(g, (hipStream_t)stream));
 }
 
+FP8BS_EXPORT int fp8_gemm_blockscaled_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                            const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                            const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1,
+                                            int scale_mode, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                            int accum, void* stream) {
+    if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
+    if (scale_mode != FP8BS_SCALE_FP32 && scale_mode != FP8BS_SCALE_POW2) return FP8BS_ERR_ARG;
+    if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
+        return FP8BS_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_ARG;
+    if (M > 0 && N > 0 && (!q || !s || (K > 0 && (!a || !sa || !b || !sb)))) return FP8BS_ERR_ARG;
+    if (K % 128 != 0 || N % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (lda < K || ldb < K || ldq < N || ldsa < M || lds < M) return FP8BS_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(q, 4) || !aligned(sa, 4) || !aligned(sb, 4) ||
+        !aligned(s, 4) || (K > 0 && (lda % 16 != 0 || ldb % 16 != 0)) || ldq % 4 != 0)
+        return FP8BS_ERR_ALIGN;
+    if (M == 0 || N == 0) return FP8BS_OK;
+    if (int r = check_device()) return r;
+    fp8bs::GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.lda = lda;
+    g.sa = sa;
+    g.ldsa = ldsa;
+    g.b = b;
+    g.ldb = ldb;
+    g.sb = sb;
+    g.bscale_kind = bscale_kind;
+    g.sb_s0 = sb_s0;
+    g.sb_s1 = sb_s1;
+    g.d = q;
+    g.ldd = ldq;
+    g.out_f32 = 0;
+    g.out_quant = scale_mode == FP8BS_SCALE_POW2 ? 2 : 1;
+    g.qs = s;
+    g.qlds = lds;
+    g.accum = accum;
+    g.splits = 1;
+    return hip_status(fp8bs::launch_gemm(g, (hipStream_t)stream));
+}
+
 FP8BS_EXPORT int fp8_grouped_gemm(int G, int64_t rows_bound, int64_t N, int64_t K, const int32_t* offsets,
                                   const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
                                   const float* sb, void* d, int64_t ldd, int out_dtype, int accum,

@@ -157,6 +157,8 @@ struct Tile {
     int64_t ldb;
     const float* sb;
     int64_t sb_s0, sb_s1;
+    float* qs;  // fused 1x128 quantisation of the output: scales qs[(n/128)*qlds + m]
+    int64_t qlds;
 };
 
 // The 8 XCDs each take a contiguous range of the tile list (the hardware
@@ -523,10 +525,10 @@ __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm,
 // ==== epilogue ===========================================================================
 
 // Store four consecutive columns n..n+3 of row m (masked at the edges).
-template <int OUT_F32>
+template <int OUT>
 __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t n, int64_t n_end, float v0,
                                        float v1, float v2, float v3) {
-    if (OUT_F32) {
+    if (OUT) {
         float* p = (float*)d + m * ldd + n;
         if (n + 4 <= n_end) {
             *(float4*)p = make_float4(v0, v1, v2, v3);
@@ -567,7 +569,10 @@ __device__ __forceinline__ void put4(float* ep, int row, int col, float v0, floa
     *(float4*)&ep[row * Epi<SH>::LD + col] = make_float4(v0, v1, v2, v3);
 }
 
-template <int SH, int OUT_F32>
+// OUT: 0 bf16, 1 fp32, 2 / 3 the bf16 result quantised in 1x128 groups
+// along n with FP32 / power-of-two scales (the tile's 128 columns are one
+// group of every row), codes to d, scales to T.qs.
+template <int SH, int OUT>
 __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T, void* d, int64_t ldd) {
     constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     constexpr int LPR = BN / 4;               // lanes per row
@@ -575,16 +580,38 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
     const int t = threadIdx.x;
     const int col = (t % LPR) * 4;
     const int64_t n = T.n0 + col;
+    if constexpr (OUT <= 1) {
 #pragma unroll 4
-    for (int r = t / LPR; r < BM; r += RPI) {
-        const int64_t m = T.m0 + r;
-        if (m >= T.m_end || n >= T.n_end) continue;
-        const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
-        store4<OUT_F32>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
+        for (int r = t / LPR; r < BM; r += RPI) {
+            const int64_t m = T.m0 + r;
+            if (m >= T.m_end || n >= T.n_end) continue;
+            const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
+            store4<OUT>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
+        }
+    } else {
+        static_assert(BN == 128 && LPR == 32, "one 1x128 group per tile row, 32 lanes per row");
+        // Every lane runs every pass (the 32-lane reductions need them all);
+        // only the stores are masked.
+        for (int r = t / LPR; r < BM; r += RPI) {
+            const int64_t m = T.m0 + r;
+            const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
+            const uint32_t b0 = f32_to_bf16_bits(v.x), b1 = f32_to_bf16_bits(v.y);
+            const uint32_t b2 = f32_to_bf16_bits(v.z), b3 = f32_to_bf16_bits(v.w);
+            uint32_t am = max(max(b0 & 0x7FFFu, b1 & 0x7FFFu), max(b2 & 0x7FFFu, b3 & 0x7FFFu)) << 16;
+            am = row16_max(am);
+            am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+            const GroupScale gs = group_scale(am, OUT == 3);
+            const uint32_t codes = pack4(bf16_lo(b0) * gs.inv, bf16_lo(b1) * gs.inv, bf16_lo(b2) * gs.inv,
+                                         bf16_lo(b3) * gs.inv);
+            if (m < T.m_end) {
+                *(uint32_t*)((uint8_t*)d + m * ldd + n) = codes;
+                if (col == 0) T.qs[(T.n0 >> 7) * T.qlds + m] = gs.s;
+            }
+        }
     }
 }
 
-template <int SH, int OUT_F32>
+template <int SH, int OUT>
 __device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T, int wm, int wn, int lane,
                                           void* d, int64_t ldd, uint8_t* smem) {
     float* ep = (float*)smem;
@@ -597,11 +624,11 @@ __device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T
                 put4<SH>(ep, wm * 64 + 32 * i + (lane & 31), wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5),
                          acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     __syncthreads();
-    write_tile_image<SH, OUT_F32>(ep, T, d, ldd);
+    write_tile_image<SH, OUT>(ep, T, d, ldd);
     __syncthreads();  // the stages may be refilled by a following tile
 }
 
-template <int SH, int OUT_F32>
+template <int SH, int OUT>
 __device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& T, int wm, int wn, int lane,
                                             void* d, int64_t ldd, uint8_t* smem) {
     float* ep = (float*)smem;
@@ -612,13 +639,13 @@ __device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& 
             put4<SH>(ep, wm * 64 + 16 * i + (lane & 15), wn * 64 + 16 * j + 4 * (lane >> 4), acc[i][j][0],
                      acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     __syncthreads();
-    write_tile_image<SH, OUT_F32>(ep, T, d, ldd);
+    write_tile_image<SH, OUT>(ep, T, d, ldd);
     __syncthreads();
 }
 
 // ==== one tile: pipelined K loop, then the store ==============================================
 
-template <int ACC, int SH, int KIND, int OUT_F32>
+template <int ACC, int SH, int KIND, int OUT>
 __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, void* d, int64_t ldd,
                                          uint8_t* smem) {
     constexpr int S = Shape<SH>::STAGES;
@@ -702,14 +729,14 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     wait_and_barrier<0>();  // the LDS stages may be reused by a following tile
 
     if constexpr (ACC == 0)
-        store_f32<SH, OUT_F32>(acc, T, wm, wn, lane, d, ldd, smem);
+        store_f32<SH, OUT>(acc, T, wm, wn, lane, d, ldd, smem);
     else
-        store_mfma8<SH, OUT_F32>(acc, T, wm, wn, lane, d, ldd, smem);
+        store_mfma8<SH, OUT>(acc, T, wm, wn, lane, d, ldd, smem);
 }
 
 // ==== kernels ==========================================================================
 
-template <int ACC, int KIND, int OUT_F32, bool SPLIT>
+template <int ACC, int KIND, int OUT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t ntiles = tiles_m * tiles_n;
@@ -732,6 +759,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
     T.sb = p.sb;
     T.sb_s0 = p.sb_s0;
     T.sb_s1 = p.sb_s1;
+    T.qs = p.qs;
+    T.qlds = p.qlds;
 
     const int64_t groups = p.K / 128;
     if (SPLIT) {
@@ -740,12 +769,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
         const int64_t g1 = g0 + per < groups ? g0 + per : groups;
         run_tile<ACC, 0, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
     } else {
-        run_tile<ACC, 0, KIND, OUT_F32>(T, 0, groups, p.d, p.ldd, smem);
+        run_tile<ACC, 0, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
 
 // Grouped: workgroup (expert e, n-tile) walks the expert's m-tiles.
-template <int ACC, int KIND, int OUT_F32>
+template <int ACC, int KIND, int OUT>
 __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -768,7 +797,7 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     T.sb_s1 = p.sb_s1;
     for (int64_t m0 = r0; m0 < r1; m0 += Shape<0>::BM) {
         T.m0 = m0;
-        run_tile<ACC, 0, KIND, OUT_F32>(T, 0, p.K / 128, p.d, p.ldd, smem);
+        run_tile<ACC, 0, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
     }
 }
 
@@ -792,7 +821,7 @@ __device__ __forceinline__ int64_t expert_first_group(const int32_t* __restrict_
     return total;
 }
 
-template <int ACC, int OUT_F32>
+template <int ACC, int OUT>
 __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t per = tiles_m * tiles_n;
@@ -817,12 +846,12 @@ __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t t
     T.sb = p.sb;
     T.sb_s0 = p.sb_s0;
     T.sb_s1 = 0;
-    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT_F32 ? 4 : 2);
-    run_tile<ACC, 0, 1, OUT_F32>(T, g0, g1, d, p.ldd, smem);
+    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT ? 4 : 2);
+    run_tile<ACC, 0, 1, OUT>(T, g0, g1, d, p.ldd, smem);
 }
 
 // Sum split-K partials in split order and convert.
-template <int OUT_F32>
+template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
                                                             int64_t M, int64_t N, int64_t ws_ld,
                                                             void* __restrict__ d, int64_t ldd) {
@@ -838,7 +867,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         s.z += v.z;
         s.w += v.w;
     }
-    store4<OUT_F32>(d, ldd, m, n, N, s.x, s.y, s.z, s.w);
+    store4<OUT>(d, ldd, m, n, N, s.x, s.y, s.z, s.w);
 }
 
 // ==== host side ==========================================================================
@@ -860,9 +889,9 @@ size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
     return (size_t)s * (size_t)M * (size_t)((N + 3) / 4 * 4) * sizeof(float);
 }
 
-template <int ACC, int KIND, int OUT_F32, bool SPLIT>
+template <int ACC, int KIND, int OUT, bool SPLIT>
 static void launch_dense(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, int64_t wgs, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<ACC, KIND, OUT_F32, SPLIT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g,
+    hipLaunchKernelGGL((gemm_kernel<ACC, KIND, OUT, SPLIT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g,
                        tiles_m, tiles_n);
 }
 
@@ -870,7 +899,7 @@ template <int ACC>
 static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
     const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
-    if (g.splits > 1) {
+    if (g.splits > 1 && !g.out_quant) {
         const int64_t wgs = tiles_m * tiles_n * g.splits;
         if (g.bscale_kind == 0)
             launch_dense<ACC, 0, 1, true>(g, tiles_m, tiles_n, wgs, st);
@@ -889,6 +918,20 @@ static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
         return hipGetLastError();
     }
     const int64_t wgs = tiles_m * tiles_n;
+    if (g.out_quant) {
+        if (g.bscale_kind == 0) {
+            if (g.out_quant == 1)
+                launch_dense<ACC, 0, 2, false>(g, tiles_m, tiles_n, wgs, st);
+            else
+                launch_dense<ACC, 0, 3, false>(g, tiles_m, tiles_n, wgs, st);
+        } else {
+            if (g.out_quant == 1)
+                launch_dense<ACC, 1, 2, false>(g, tiles_m, tiles_n, wgs, st);
+            else
+                launch_dense<ACC, 1, 3, false>(g, tiles_m, tiles_n, wgs, st);
+        }
+        return hipGetLastError();
+    }
     if (g.bscale_kind == 0) {
         if (g.out_f32)
             launch_dense<ACC, 0, 1, false>(g, tiles_m, tiles_n, wgs, st);

@@ -51,6 +51,12 @@ struct GemmArgs {
     void* d;
     int64_t ldd;
     int out_f32;  // 0 bf16, 1 fp32
+    // fused quantisation of the bf16 result in 1x128 groups along n
+    // (0 off, 1 FP32 scales, 2 power-of-two scales): codes to d, scales to
+    // qs[(n/128)*qlds + m]
+    int out_quant;
+    float* qs;
+    int64_t qlds;
     int accum;    // 0 FP32-accurate group partials (f16 matrix cores), 1 FP8 matrix cores
     // split-K (dense only): partials in `ws`, row stride ws_ld floats
     float* ws;

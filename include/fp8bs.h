@@ -307,6 +307,31 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t *a,
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * fp8_gemm_blockscaled_quant -- the block-scaled GEMM with its output
+ * quantised in the epilogue, so a layer's activation leaves the kernel that
+ * produces it already in FP8 and never makes a BF16 round trip through HBM
+ * (the pages name that round trip -- read BF16 back, quantise, write FP8,
+ * read again for the next MMA -- as the cost to remove: [hacks-368261],
+ * passages on fusing FP8 casting with memory access).  The result is
+ * exactly what fp8_gemm_blockscaled with FP8BS_OUT_BF16 followed by
+ * fp8_quant_tile(FP8BS_AXIS_ROW, scale_mode) of that bf16 matrix would give:
+ *   q   codes [M][ldq]; s[g*lds + m] the scale of row m, columns 128g..128g+127.
+ * Other arguments as fp8_gemm_blockscaled.  N must be a multiple of 128.
+ * The K loop is never split (long-K shapes with few output tiles run at
+ * lower occupancy than in fp8_gemm_blockscaled).
+ * Alignment: q 4-byte aligned, ldq a multiple of 4; s 4-byte aligned;
+ * ldq >= N; lds >= M; otherwise as fp8_gemm_blockscaled.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP.
+ */
+int fp8_gemm_blockscaled_quant(int64_t M, int64_t N, int64_t K,
+                               const uint8_t *a, int64_t lda, const float *sa,
+                               int64_t ldsa, const uint8_t *b, int64_t ldb,
+                               const float *sb, int bscale_kind, int64_t sb_s0,
+                               int64_t sb_s1, int scale_mode, uint8_t *q,
+                               int64_t ldq, float *s, int64_t lds, int accum,
+                               void *stream);
+
+/*
  * fp8_grouped_gemm -- the block-scaled GEMM for a group of MoE experts
  * (expert GEMMs in FP8, [why-be-59061] passage on the activation gradient
  * before the MoE down-projection; few, memory-bound tokens per expert in

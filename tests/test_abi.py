@@ -26,6 +26,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
               "fp8_grouped_gemm_strided", "fp8_quant_tile_grouped_col", "fp8_grouped_gemm_kgrouped",
+              "fp8_gemm_blockscaled_quant",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -143,6 +144,24 @@ def _gemm(**kw):
 ])
 def test_gemm_validation(kw, want):
     assert _gemm(**kw) == want
+
+
+def _gq(**kw):
+    a = dict(M=256, N=256, K=512, a=FAKE, lda=512, sa=FAKE, ldsa=256, b=FAKE, ldb=512, sb=FAKE, kind=0, s0=4, s1=1,
+             mode=0, q=FAKE, ldq=256, s=FAKE, lds=256, acc=0)
+    a.update(kw)
+    return bs.lib().fp8_gemm_blockscaled_quant(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["ldsa"], a["b"],
+                                               a["ldb"], a["sb"], a["kind"], a["s0"], a["s1"], a["mode"], a["q"],
+                                               a["ldq"], a["s"], a["lds"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kind=2), ARG), (dict(mode=2), ARG), (dict(acc=3), ARG), (dict(q=None), ARG), (dict(s=None), ARG),
+    (dict(ldq=128), ARG), (dict(lds=100), ARG), (dict(N=200, ldq=256), SHAPE), (dict(K=500, lda=512, ldb=512), SHAPE),
+    (dict(q=FAKE + 2), ALIGN), (dict(ldq=258), ALIGN), (dict(s=FAKE + 1), ALIGN), (dict(M=0), OK),
+])
+def test_gemm_quant_validation(kw, want):
+    assert _gq(**kw) == want
 
 
 def test_workspace_query():

@@ -233,3 +233,45 @@ def test_expert_backward_full_size(hip, orc, accum):
     mi, ni = _sampled(np.random.default_rng(3), 2048, 7168)
     r, rabs = sampled(orc, wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0, mi, ni)
     check(out_f64(dw)[mi, ni], r, rabs, 1, accum, 64, f"expert wgrad full size accum={accum}")
+
+
+@ACCUMS_POW2
+@pytest.mark.parametrize("kind", [0, 1], ids=["block", "tile"])
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
+def test_gemm_fused_quant(hip, orc, mode, kind, accum):
+    """The GEMM with its output quantised 1x128 in the epilogue equals the
+    GEMM's bf16 output quantised by fp8_quant_tile, and that quantisation of
+    the bf16 output equals the oracle's, bit for bit: ragged M (300 rows),
+    N = 384, K = 1024, both B-scale kinds."""
+    if accum == 2 and mode == 0:
+        pytest.skip("the scaled-MFMA mode takes power-of-two scales only")
+    X = inputs.random_bf16(111, (300, 1024))
+    qx, sx = hip.fp8_quant_tile(dev_bf16(X), hip.AXIS_ROW, mode)
+    if kind == 0:
+        W = inputs.random_bf16(112, (384, 1024), sd=0.02, outliers=False)
+        qw, sw, _ = hip.fp8_quant_block(dev_bf16(W), mode)
+        s0, s1 = sw.shape[1], 1
+    else:
+        # per-column B scales: quantise W^T in 128x1 groups along K
+        W = inputs.random_bf16(112, (1024, 384), sd=0.02, outliers=False)
+        qw, sw = hip.fp8_quant_tile(dev_bf16(W), hip.AXIS_COL, mode)
+        s0, s1 = sw.shape[1], 0
+    q, s = hip.fp8_gemm_blockscaled_quant(qx, sx, qw, sw, kind, s0, s1, mode, accum=accum)
+    y = hip.fp8_gemm_blockscaled(qx, sx, qw, sw, kind, s0, s1, hip.OUT_BF16, accum=accum)
+    q2, s2 = hip.fp8_quant_tile(y, hip.AXIS_ROW, mode)
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+    wq, ws = orc.quant_tile(host(y), 0, mode)
+    np.testing.assert_array_equal(host(q), wq)
+    np.testing.assert_array_equal(host(s), ws)
+
+
+def test_gemm_fused_quant_full_size(hip, orc):
+    """Dense Fprop at its real size: the fused epilogue quantisation equals
+    quantising the bf16 output in a separate pass, every code and scale."""
+    d = workload("dense_fprop")
+    qx, sx = hip.fp8_quant_tile(dev_bf16(d["X"]), hip.AXIS_ROW, 0)
+    qw, sw, _ = hip.fp8_quant_block(dev_bf16(d["W"]), 0)
+    q, s = hip.fp8_gemm_blockscaled_quant(qx, sx, qw, sw, 0, sw.shape[1], 1, 0)
+    y = hip.linear_fprop(qx, sx, qw, sw, hip.OUT_BF16)
+    q2, s2 = hip.fp8_quant_tile(y, hip.AXIS_ROW, 0)
+    assert torch.equal(q, q2) and torch.equal(s, s2)
