@@ -28,22 +28,26 @@
 //  the matrix core itself, so there is no promotion step on the VALU.
 //
 // All: the MFMA's first operand is the B (weight) tile and its second the
-// A (activation) tile, so each result sub-tile is D^T and every lane ends
-// with runs of four consecutive output columns of one row (one 8-byte bf16
-// or 16-byte fp32 store) and needs one activation scale per sub-tile.  Each
-// lane's k positions depend only on its lane index, identically for both
-// operands, so whatever order the hardware pairs elements in, equal k meet.
+// A (activation) tile, so each result sub-tile is D^T: every lane holds runs
+// of four consecutive output columns of one row and needs one activation
+// scale per sub-tile.  Each lane's k positions depend only on its lane
+// index, identically for both operands, so whatever order the hardware
+// pairs elements in, equal k meet.
 //
 // Staging: 512 threads (two waves per SIMD).  Each K group of both tiles
 // goes global -> LDS with global_load_lds_dwordx4 (no register staging:
 // lane i of a wave instruction lands at LDS base + 16*i, so each
 // instruction fills 8 rows of 128 B), the group's scales with 4-byte
-// global_load_lds (see dma16).  Tiles sit in LDS as FP8 codes, rows of 128 B whose
-// 16-byte chunks are XOR-swizzled by (row ^ row>>3) & 7 -- lanes fetch the
-// permuted chunk of their row, so coalescing is unchanged and the fragment
-// reads of 8 or 16 consecutive rows hit distinct banks.  STAGES groups are
-// in flight; one barrier per group both publishes the landed group and
-// frees the stage the next issue overwrites.
+// global_load_lds (see dma16s, Stager).  Tiles sit in LDS as FP8 codes,
+// rows of 128 B whose 16-byte chunks are XOR-swizzled by (row ^ row>>3) & 7
+// -- lanes fetch the permuted chunk of their row, so coalescing is unchanged
+// and the fragment reads of 8 or 16 consecutive rows hit distinct banks.
+// STAGES groups are in flight; one barrier per group both publishes the
+// landed group and frees the stage the next issue overwrites.
+//
+// Epilogue: the tile goes through a row-major fp32 image in the freed stage
+// memory and leaves in whole row segments (bf16, fp32, or -- fused -- the
+// bf16 result quantised 1x128 along n, one group per tile row).
 #include <type_traits>
 
 #include "device.h"
@@ -103,22 +107,14 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // kernel orders them itself with wait_and_barrier.  The instructions have
 // no register results.  M0 holds the wave-uniform LDS base; lane i's data
 // lands at M0 + size*i.  M0 is a reserved register the compiler never
-// assigns in these kernels, so it is not listed as clobbered.
+// assigns in these kernels, so it is not listed as clobbered.  The SADDR
+// form is used: a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset, so the per-lane offsets stay fixed over the K loop and only
+// the scalar base advances.
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
     return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory");
-}
-
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gptr) : "memory");
-}
-
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
-// byte offset (the instruction's SADDR form): the per-lane offsets stay
-// fixed over the K loop and only the scalar base advances.
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
@@ -252,90 +248,9 @@ struct Stager {
 // v_mfma_f32_32x32x16_f16: lane l feeds row l%32 of its operand with 8
 // values per k-step.  Lane l reads the 16-byte chunk c = 2q + l/32 of its
 // row (q = 0..3) and widens it to 16 f16: the first 8 feed k-step 2q, the
-// last 8 k-step 2q+1.
+// last 8 k-step 2q+1.  lds16 reads a chunk of a swizzled tile row; widen16
+// converts its 16 codes exactly (v_cvt_scalef32_pk_f16_fp8, scale 1).
 
-__device__ __forceinline__ void f16_pair(const uint8_t* tile, int row, int chunk, v8h& lo, v8h& hi) {
-    const uint4 v = *(const uint4*)(tile + f8_off(row, chunk));
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    v2h p[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
-        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        lo[2 * i] = p[i][0];
-        lo[2 * i + 1] = p[i][1];
-        hi[2 * i] = p[4 + i][0];
-        hi[2 * i + 1] = p[4 + i][1];
-    }
-}
-
-// acc[i][j]: 32x32 sub-tile (m-sub i, n-sub j) of this wave, D^T layout:
-// register r of lane l is n = 32j + 8(r/4) + 4(l/32) + r%4, m = 32i + l%32.
-template <int SH, int KIND>
-__device__ __forceinline__ void compute_f32(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
-                                            int lane, int m_valid, v16f (&acc)[2][2]) {
-    const uint8_t* la = stage + Lds<SH>::A;
-    const uint8_t* lb = stage + Lds<SH>::B;
-    const float* lsa = (const float*)(stage + Lds<SH>::SA);
-    const float* lsb = (const float*)(stage + Lds<SH>::SB);
-    const int mbase = wm * 64, nbase = wn * 64;
-    if (mbase >= m_valid) return;  // this wave's rows are all past the end
-    const float sbk = KIND == 0 ? lsb[nbase >> 7] : 0.f;
-
-    v16f p[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) p[i][j][r] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const int chunk = 2 * q + (lane >> 5);
-        v8h a0[2], a1[2], b0[2], b1[2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) f16_pair(la, mbase + 32 * i + (lane & 31), chunk, a0[i], a1[i]);
-#pragma unroll
-        for (int j = 0; j < 2; j++) f16_pair(lb, nbase + 32 * j + (lane & 31), chunk, b0[j], b1[j]);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], p[i][j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], p[i][j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const float sam = lsa[mbase + 32 * i + (lane & 31)];
-        const float c = KIND == 0 ? sam * sbk : sam;
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            if (KIND == 0) {
-                acc[i][j] += p[i][j] * c;
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const v4f sbn = *(const v4f*)(lsb + nbase + 32 * j + 8 * q + 4 * (lane >> 5));
-#pragma unroll
-                    for (int e = 0; e < 4; e++) acc[i][j][4 * q + e] += (p[i][j][4 * q + e] * c) * sbn[e];
-                }
-            }
-        }
-    }
-}
-
-// Block-scale kind, software-pipelined: the fragments of k-chunk q+1 are
-// read from LDS while chunk q is widened and multiplied, and the partials
-// of the previous group are promoted at the start of this group, each
-// sub-tile's promotion just before the first MFMA that reuses its
-// registers, so the promotion FMAs run beside this group's MFMAs.  p and cp
-// carry the previous group's partials and scale factors (zero before the
-// first group).
 __device__ __forceinline__ uint4 lds16(const uint8_t* tile, int row, int chunk) {
     return *(const uint4*)(tile + f8_off(row, chunk));
 }
@@ -357,6 +272,80 @@ __device__ __forceinline__ void widen16(const uint4 v, v8h& lo, v8h& hi) {
     }
 }
 
+// Per-column (tile-kind) B scales, as Wgrad uses: acc += (P_g * sa[m]) *
+// sb[n], the partials promoted at the end of the group.  The fragments of
+// k-chunk q+1 are read from LDS while chunk q is widened and multiplied.
+// acc[i][j]: 32x32 sub-tile (m-sub i, n-sub j) of this wave, D^T layout:
+// register r of lane l is n = 32j + 8(r/4) + 4(l/32) + r%4, m = 32i + l%32.
+template <int SH>
+__device__ __forceinline__ void compute_f32_tile(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
+                                                 v16f (&acc)[2][2]) {
+    const uint8_t* la = stage + Lds<SH>::A;
+    const uint8_t* lb = stage + Lds<SH>::B;
+    const float* lsa = (const float*)(stage + Lds<SH>::SA);
+    const float* lsb = (const float*)(stage + Lds<SH>::SB);
+    const int mbase = wm * 64, nbase = wn * 64;
+    const int r = lane & 31, h = lane >> 5;
+    if (mbase >= m_valid) return;  // this wave's rows are all past the end
+
+    uint4 ra[2], rb[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) ra[i] = lds16(la, mbase + 32 * i + r, h);
+#pragma unroll
+    for (int j = 0; j < 2; j++) rb[j] = lds16(lb, nbase + 32 * j + r, h);
+    v16f p[2][2];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint4 na[2], nb[2];
+        if (q < 3) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) na[i] = lds16(la, mbase + 32 * i + r, 2 * (q + 1) + h);
+#pragma unroll
+            for (int j = 0; j < 2; j++) nb[j] = lds16(lb, nbase + 32 * j + r, 2 * (q + 1) + h);
+        }
+        v8h a0[2], a1[2], b0[2], b1[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) widen16(ra[i], a0[i], a1[i]);
+#pragma unroll
+        for (int j = 0; j < 2; j++) widen16(rb[j], b0[j], b1[j]);
+        const v16f zero = {};
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], q == 0 ? zero : p[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], p[i][j], 0, 0, 0);
+        if (q < 3) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) ra[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < 2; j++) rb[j] = nb[j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const float sam = lsa[mbase + 32 * i + r];
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const v4f sbn = *(const v4f*)(lsb + nbase + 32 * j + 8 * q + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[i][j][4 * q + e] += (p[i][j][4 * q + e] * sam) * sbn[e];
+            }
+    }
+}
+
+// Block-scale kind (Fprop, Dgrad, grouped), software-pipelined: the
+// fragments of k-chunk q+1 are read from LDS while chunk q is widened and
+// multiplied, and the partials of the previous group are promoted at the
+// start of this group, each sub-tile's promotion just before the first MFMA
+// that reuses its registers, so the promotion FMAs run beside this group's
+// MFMAs.  p and cp carry the previous group's partials and scale factors
+// (zero before the first group).
 template <int SH>
 __device__ __forceinline__ void compute_f32_block(const uint8_t* stage, int wm, int wn, int lane,
                                                   v16f (&acc)[2][2], v16f (&p)[2][2], float (&cp)[2]) {
@@ -707,7 +696,7 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         if constexpr (ACC == 0 && KIND == 0) {
             if (wm * 64 < m_valid) compute_f32_block<SH>(stage, wm, wn, lane, acc, pp, cp);
         } else if constexpr (ACC == 0) {
-            compute_f32<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+            compute_f32_tile<SH>(stage, wm, wn, lane, m_valid, acc);
         } else {
             if constexpr (ACC == 1)
                 compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
