@@ -275,3 +275,35 @@ def test_gemm_fused_quant_full_size(hip, orc):
     y = hip.linear_fprop(qx, sx, qw, sw, hip.OUT_BF16)
     q2, s2 = hip.fp8_quant_tile(y, hip.AXIS_ROW, 0)
     assert torch.equal(q, q2) and torch.equal(s, s2)
+
+
+@ACCUMS_POW2
+def test_strided_operands_and_output(hip, orc, accum):
+    """Operands read through leading dimensions larger than K and outputs
+    written into a wider matrix give the same bits as the contiguous call
+    and leave the bytes outside the view alone; shapes include one row, one
+    K group and a ragged N (M = 1, 129; K = 128, 640; N = 136)."""
+    rng = np.random.default_rng(17)
+    table = orc.decode_table()
+    finite = np.array([c for c in range(256) if not np.isnan(table[c])], np.uint8)
+    for M, K in [(1, 128), (129, 640)]:
+        N = 136
+        a = rng.choice(finite, (M, K))
+        b = rng.choice(finite, (N, K))
+        sa = (2.0 ** rng.integers(-4, 4, (K // 128, M))).astype(np.float32)
+        sb = (2.0 ** rng.integers(-4, 4, ((N + 127) // 128, K // 128))).astype(np.float32)
+        ref = hip.fp8_gemm_blockscaled(dev(a), dev(sa), dev(b), dev(sb), 0, K // 128, 1, 1, accum=accum)
+        A = torch.zeros((M, K + 144), dtype=torch.uint8, device="cuda")
+        A[:, 16:16 + K] = dev(a)
+        B = torch.zeros((N, K + 32), dtype=torch.uint8, device="cuda")
+        B[:, :K] = dev(b)
+        SA = torch.zeros((K // 128, M + 7), dtype=torch.float32, device="cuda")
+        SA[:, :M] = dev(sa)
+        D = torch.full((M, N + 12), -3.0, dtype=torch.float32, device="cuda")
+        hip.fp8_gemm_blockscaled(A[:, 16:16 + K], SA[:, :M], B[:, :K], dev(sb), 0, K // 128, 1, 1,
+                                 d=D[:, 4:4 + N], accum=accum)
+        assert torch.equal(D[:, 4:4 + N], ref)
+        assert torch.all(D[:, :4] == -3.0).item() and torch.all(D[:, 4 + N:] == -3.0).item()
+        r = orc.gemm(a, sa, b, sb, 0, K // 128, 1)
+        rabs = orc.gemm(a & 0x7F, sa, b & 0x7F, sb, 0, K // 128, 1)
+        check(out_f64(ref), r, rabs, 1, accum, K // 128, f"strided M={M} K={K} accum={accum}")
