@@ -414,15 +414,17 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 // amax, and the 16 lanes write the 128 new codes as one 128-byte run of
 // the transposed output.
 
-// Exact values of the four E4M3 codes packed in a dword (low byte first).
+// Exact values of the four E4M3 codes packed in a dword (low byte first):
+// v_cvt_scalef32_pk_f32_fp8 with scale 1 (every finite code is exact in
+// fp32; checked over all codes by the round-trip test of the re-tiling).
 __device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-    const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-    v[0] = (float)lo[0];
-    v[1] = (float)lo[1];
-    v[2] = (float)hi[0];
-    v[3] = (float)hi[1];
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+    v[0] = lo[0];
+    v[1] = lo[1];
+    v[2] = hi[0];
+    v[3] = hi[1];
 }
 
 template <bool POW2>
@@ -469,10 +471,10 @@ __global__ __launch_bounds__(256) void requant_col_kernel(const uint8_t* __restr
         decode4(v.y, d);
 #pragma unroll
         for (int i = 0; i < 4; i++) x[4 + i] = d[i] * rs[4 + i];
-        uint32_t am = 0;
+        float fam = 0.f;  // max |x| (non-negative, so its bits order like its values)
 #pragma unroll
-        for (int i = 0; i < 8; i++) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-        am = row16_max(am);
+        for (int i = 0; i < 8; i++) fam = fmaxf(fam, fabsf(x[i]));
+        const uint32_t am = row16_max(__float_as_uint(fam));
         const GroupScale gs = group_scale(am, POW2);
         const uint2 codes = make_uint2(pack4(x[0] * gs.inv, x[1] * gs.inv, x[2] * gs.inv, x[3] * gs.inv),
                                        pack4(x[4] * gs.inv, x[5] * gs.inv, x[6] * gs.inv, x[7] * gs.inv));

@@ -128,3 +128,26 @@ def test_quant_dual_full_size(hip, orc):
     np.testing.assert_array_equal(host(sr), wsr)
     np.testing.assert_array_equal(host(qc), wqc)
     np.testing.assert_array_equal(host(sc), wsc)
+
+
+def test_requant_every_code_round_trips(hip, orc):
+    """Each column holds the 254 finite codes (in a different order per
+    column) with unit row scales; the largest magnitude, 448, makes the new
+    scale 1, so re-tiling must give back every code exactly -- the device
+    decode of every finite code is exact."""
+    table = orc.decode_table()
+    finite = np.array([c for c in range(256) if not np.isnan(table[c])], np.uint8)
+    rng = np.random.default_rng(9)
+    q = np.zeros((256, 128), np.uint8)
+    for c in range(128):
+        q[:254, c] = rng.permutation(finite)
+    s = np.ones((1, 256), np.float32)
+    qt, st = hip.fp8_requant_col(dev(q), dev(s), 0)
+    wqt, wst = orc.requant_col(q, s, 0)
+    np.testing.assert_array_equal(host(qt), wqt)
+    np.testing.assert_array_equal(host(st), wst)
+    # the group holding 0x7E / 0xFE has scale 1: its codes come back unchanged
+    for c in range(128):
+        for g in range(2):
+            if st[g, c] == 1.0:
+                np.testing.assert_array_equal(host(qt)[c, 128 * g:128 * g + 128], q[128 * g:128 * g + 128, c])
