@@ -1,6 +1,6 @@
 """Benchmark of the fine-grained FP8 linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum fp32|mfma8]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum mfma8|fp32]
     python bench.py --traffic-probe     # plain copy of known size, for counter scaling
     python bench.py --workload expert_backward|grouped_upproj|decode_grouped
     python bench.py --library-ceiling   # vendor GEMMs on the dense shape, for context
@@ -26,9 +26,12 @@ hot path over that batch, inputs already in HBM:
     quantise X in 1x128 tiles  (fp8_quant_tile, FP32 scales)
     quantise W in 128x128 blocks (fp8_quant_block, FP32 scales)
     Y = X W^T, block-scaled FP8 GEMM with per-128 FP32 promotion, bf16 out.
-The GEMM's accumulation mode is --accum (fp32: exact group partials on the
-f16 matrix cores; mfma8: group partials from the FP8 matrix cores); the
-other mode's GEMM is timed as well and reported under `gemm_modes`.
+The GEMM's accumulation mode is --accum: mfma8 (the default) forms each
+128-element group partial on the FP8 matrix cores and promotes it in FP32
+registers -- the pages' scheme -- and meets the bf16 gate on this workload;
+fp32 forms the partials exactly on the f16 matrix cores.  `gemm_modes`
+reports both, and the power-of-two-scale mode (the same step with
+power-of-two scales, the scales applied inside the FP8 MFMA).
 
 Prints one JSON line.  `value` is the step's GEMM FLOPs over the step time
 (quantisation included); `roofline` covers the dominant kernel (the GEMM),
@@ -52,6 +55,8 @@ M, N, K = 4096, 18432, 7168
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_fprop_traffic.txt")
+# the kernel one dense-Fprop GEMM call launches, per accumulation mode
+GEMM_KERNEL = {"mfma8": "gemm_wide_kernel<1, 0, 0>", "fp32": "gemm_kernel<0, 0, 0, 0, false>"}
 KERNEL_SOURCES = ["block_scaled_gemm_amd/csrc/gemm.hip", "block_scaled_gemm_amd/csrc/device.h"]
 
 
@@ -329,8 +334,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--accum", choices=["fp32", "mfma8"], default="fp32",
-                    help="GEMM accumulation: exact group partials (fp32) or FP8 matrix cores (mfma8)")
+    ap.add_argument("--accum", choices=["mfma8", "fp32"], default=None,
+                    help="GEMM accumulation: FP8 matrix cores (mfma8) or exact group partials (fp32); "
+                         "default: mfma8 for dense_fprop, fp32 elsewhere (the fastest mode that meets the "
+                         "output's gate on that workload)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only a plain copy of known size (counter scaling)")
     ap.add_argument("--library-ceiling", action="store_true",
@@ -338,6 +345,8 @@ def main():
     ap.add_argument("--workload", default="dense_fprop",
                     choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped", "moe_backward"])
     args = ap.parse_args()
+    if args.accum is None:
+        args.accum = "mfma8" if args.workload == "dense_fprop" else "fp32"
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "
               "single-GPU build (no collectives); run with --gpus 1", file=sys.stderr)
@@ -358,7 +367,7 @@ def main():
     from block_scaled_gemm_amd import inputs
     accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8}[args.accum]
     other = "mfma8" if args.accum == "fp32" else "fp32"
-    kernel = f"gemm_kernel<{accum}, 0, 0, false>"
+    kernel = GEMM_KERNEL[args.accum]
 
     t_gen = time.perf_counter()
     d = inputs.dense_fprop()
@@ -407,18 +416,26 @@ def main():
     print(f"[bench] {args.steps} steps: {step_ms:.3f} ms/step (quant X {qx_ms:.3f}, quant W {qw_ms:.3f}, "
           f"gemm {gemm_ms:.3f} ms)", file=sys.stderr, flush=True)
 
-    # the same GEMM in the other accumulation mode, outside the timed steps
+    # outside the timed steps: the same GEMM in the other accumulation mode,
+    # and the power-of-two-scale mode on power-of-two quantisations of X, W
+    def gemm_time(fn):
+        fn()
+        oe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in oe:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in oe]))
+
     other_accum = bs.ACCUM_MFMA8 if accum == bs.ACCUM_FP32 else bs.ACCUM_FP32
-    oe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y,
-                            accum=other_accum)
-    for e in oe:
-        e[0].record()
-        bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16, d=y,
-                                accum=other_accum)
-        e[1].record()
-    torch.cuda.synchronize()
-    other_ms = np.mean([e[0].elapsed_time(e[1]) for e in oe])
+    other_ms = gemm_time(lambda: bs.fp8_gemm_blockscaled(qx, sx, qw, sw, bs.BSCALE_BLOCK, K // 128, 1, bs.OUT_BF16,
+                                                         d=y, accum=other_accum))
+    qx2, sx2 = bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_POW2)
+    qw2, sw2, _ = bs.fp8_quant_block(W, bs.SCALE_POW2)
+    pow2_ms = gemm_time(lambda: bs.fp8_gemm_blockscaled(qx2, sx2, qw2, sw2, bs.BSCALE_BLOCK, K // 128, 1,
+                                                        bs.OUT_BF16, d=y, accum=bs.ACCUM_MFMA8_POW2))
+    del qx2, sx2, qw2, sw2
 
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -449,6 +466,8 @@ def main():
                          "frac_fp8_peak": flops_tf(gemm_ms) / PEAK_FP8_TFLOPS},
             other: {"ms": other_ms, "TFLOP/s": flops_tf(other_ms),
                     "frac_fp8_peak": flops_tf(other_ms) / PEAK_FP8_TFLOPS},
+            "mfma8_pow2 (power-of-two scales)": {"ms": pow2_ms, "TFLOP/s": flops_tf(pow2_ms),
+                                                 "frac_fp8_peak": flops_tf(pow2_ms) / PEAK_FP8_TFLOPS},
         },
         "quantizers": {
             "quant_tile_row_X": {"ms": qx_ms, "GB/s": bx / (qx_ms * 1e-3) / 1e9,

@@ -39,7 +39,7 @@
 // lane i of a wave instruction lands at LDS base + 16*i, so each
 // instruction fills 8 rows of 128 B), the group's scales with 4-byte
 // global_load_lds (see dma16s, Stager).  Tiles sit in LDS as FP8 codes,
-// rows of 128 B whose 16-byte chunks are XOR-swizzled by (row ^ row>>3) & 7
+// rows of 128 B whose 16-byte chunks are XOR-swizzled by (row & 7) ^ (row>>3 & 1)
 // -- lanes fetch the permuted chunk of their row, so coalescing is unchanged
 // and the fragment reads of 8 or 16 consecutive rows hit distinct banks.
 // STAGES groups are in flight; one barrier per group both publishes the
@@ -64,16 +64,22 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr int THREADS = 512;
 constexpr int WAVES = THREADS / 64;
 
-// Workgroup tile shapes: 8 waves of 64 x 64 each, three K groups in flight.
-// Shape 0, 256 (m) x 128 (n), serves every launch.  (A 128 x 256 shape for
-// experts of about 128 rows measured no faster on the grouped workloads:
-// the 256-row tile reads each weight tile once per expert.)
+// Workgroup tile shapes, 8 waves each on a 4 (m) x 2 (n) wave grid.
+//  Shape 0: 256 (m) x 128 (n), waves of 64 x 64, three K groups in flight.
+//    The f16 path, split-K and the grouped kernels use it.  (A 128 x 256
+//    shape for experts of about 128 rows measured no faster on the grouped
+//    workloads: the 256-row tile reads each weight tile once per expert.)
+//  Shape 1: 256 x 256, waves of 64 x 128, two K groups in flight.  The FP8
+//    matrix-core paths of the dense GEMM use it: at the FP8 rate the
+//    staging, not the matrix core, bounds the 256 x 128 tile, and the wider
+//    tile stages a third fewer bytes and reads a quarter fewer from LDS per
+//    FLOP.  Two stages of 66 KB fill the LDS.
 template <int SH>
 struct Shape;
 template <>
 struct Shape<0> {
     static constexpr int BM = 256, BN = 128;
-    static constexpr int WGM = 4, WGN = 2;  // wave grid (m, n)
+    static constexpr int WM = 64, WN = 64;  // wave tile
     static constexpr int STAGES = 3;
     // Wave w runs on SIMD w % 4.  The two waves of a SIMD take one m-slot
     // from the top half of the tile and one from the bottom half, so a tile
@@ -83,6 +89,13 @@ struct Shape<0> {
         wm = (wave & 1) + 2 * (wave >> 2);
         wn = (wave >> 1) & 1;
     }
+};
+template <>
+struct Shape<1> {
+    static constexpr int BM = 256, BN = 256;
+    static constexpr int WM = 64, WN = 128;
+    static constexpr int STAGES = 2;
+    __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<0>::wave_grid(wave, wm, wn); }
 };
 
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
@@ -137,7 +150,12 @@ __device__ __forceinline__ void wait_and_barrier<6>() {
     asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Chunk swizzle of a tile row: (row mod 8) ^ bit 3 of the row.  The 16
+// rows of a fragment read (16 lanes per LDS cycle, 256 B over the banks)
+// fall 8 on even and 8 on odd bank halves, and each half sees 8 distinct
+// chunk positions; rows 16 apart share the swizzle, so the fragments of a
+// wave differ by constant offsets.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int f8_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 // ---- tile description and workgroup -> tile order ---------------------------------
@@ -214,6 +232,12 @@ struct Stager {
             const int w = wave - SA_INS;
             const int64_t n = T.n0 + w * 64 + lane < T.n_end ? T.n0 + w * 64 + lane : T.n_end - 1;
             vs = (uint32_t)(n - T.n0) * 4;
+        } else if (KIND == 0 && wave == SA_INS) {
+            // lane l loads the scalar of the tile's block column l (clamped
+            // to the last block column present)
+            const int64_t last = (T.n_end - 1 - T.n0) >> 7;
+            const int64_t blk = lane < last ? lane : last;
+            vs = (uint32_t)(blk * T.sb_s0 * 4);
         }
     }
 
@@ -230,15 +254,16 @@ struct Stager {
             dma16s(vb[ins], b, base + Lds<SH>::B + (ins * WAVES + wave) * 8 * 128);
         // scales: the first waves load sa (64 floats per instruction); the
         // waves after them load the B scales -- BN per-column floats (tile
-        // kind) or, block kind, the group's block scalar (every lane loads
-        // the same word; the BN/128 = 1 copies that matter sit first)
-        static_assert(KIND == 1 || BN == 128, "block kind stages one block scalar per group");
+        // kind) or, block kind, the group's BN/128 block scalars (lane l
+        // loads block column l; the copies past them land in unused words)
+        static_assert(SA_INS + (KIND == 1 ? SB_INS : 1) <= WAVES, "one scale instruction per wave");
+        static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
         if (wave < SA_INS) {
             dma4s(vs, T.sa + g * T.ldsa + T.m0, base + Lds<SH>::SA + wave * 256);
         } else if (KIND == 1 && wave < SA_INS + SB_INS) {
             dma4s(vs, T.sb + g * T.sb_s0 + T.n0, base + Lds<SH>::SB + (wave - SA_INS) * 256);
         } else if (KIND == 0 && wave == SA_INS) {
-            dma4s(0u, T.sb + (T.n0 >> 7) * T.sb_s0 + g * T.sb_s1, base + Lds<SH>::SB);
+            dma4s(vs, T.sb + (T.n0 >> 7) * T.sb_s0 + g * T.sb_s1, base + Lds<SH>::SB);
         }
     }
 };
@@ -430,42 +455,98 @@ __device__ __forceinline__ v4f mfma8_group(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Sub-tiles of one wave: MI (m) x NJ (n) of 16 x 16.
+template <int SH>
+struct Sub {
+    static constexpr int MI = Shape<SH>::WM / 16, NJ = Shape<SH>::WN / 16;
+};
+
 // acc[i][j]: 16x16 sub-tile (m-sub i, n-sub j), D^T layout: register e of
-// lane l is n = 16j + 4(l/16) + e, m = 16i + l%16.
+// lane l is n = 16j + 4(l/16) + e, m = 16i + l%16.  The fragments of the
+// wave's shorter side stay in registers while those of the longer side
+// stream past them.  A wave's WN <= 128 columns lie in one 128-column block.
 template <int SH, int KIND>
-__device__ __forceinline__ void compute_mfma8(const uint8_t* stage, const Tile& T, int64_t g, int wm, int wn,
-                                              int lane, int m_valid, v4f (&acc)[4][4]) {
+__device__ __forceinline__ void compute_mfma8(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
+                                              v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ]) {
+    constexpr int MI = Sub<SH>::MI, NJ = Sub<SH>::NJ;
     const uint8_t* la = stage + Lds<SH>::A;
     const uint8_t* lb = stage + Lds<SH>::B;
     const float* lsa = (const float*)(stage + Lds<SH>::SA);
     const float* lsb = (const float*)(stage + Lds<SH>::SB);
-    const int mbase = wm * 64, nbase = wn * 64;
+    const int mbase = wm * Shape<SH>::WM, nbase = wn * Shape<SH>::WN;
     const int c0 = 2 * (lane >> 4);
     if (mbase >= m_valid) return;
     const float sbk = KIND == 0 ? lsb[nbase >> 7] : 0.f;
 
-    v8i bf[4];
+    if constexpr (MI < NJ) {
+        // A resident: rows past m_valid are read (stale LDS) but never stored
+        v8i af[MI];
+        float c[MI];
 #pragma unroll
-    for (int j = 0; j < 4; j++) bf[j] = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
-    v4f sbn[4];
-    if (KIND == 1) {
+        for (int i = 0; i < MI; i++) {
+            const int mrow = mbase + 16 * i + (lane & 15);
+            af[i] = f8_frag(la, mrow, c0);
+            c[i] = KIND == 0 ? lsa[mrow] * sbk : lsa[mrow];
+        }
+        // Software-pipelined over the B fragments: fragment j+1 is read
+        // while column j's MFMAs run, and column j's partials are promoted
+        // after column j+1's MFMAs are issued, so neither the LDS latency
+        // nor the MFMA latency stalls the wave.
+        v8i bf = f8_frag(lb, nbase + (lane & 15), c0);
+        v4f pp[MI];
+        v4f sbp;
 #pragma unroll
-        for (int j = 0; j < 4; j++) sbn[j] = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
-    }
+        for (int j = 0; j < NJ; j++) {
+            v8i bn;
+            if (j + 1 < NJ) bn = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
+            v4f pc[MI];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (mbase + 16 * i >= m_valid) break;  // wave-uniform
-        const int mrow = mbase + 16 * i + (lane & 15);
-        const v8i af = f8_frag(la, mrow, c0);
-        const float sam = lsa[mrow];
-        const float c = KIND == 0 ? sam * sbk : sam;
+            for (int i = 0; i < MI; i++) pc[i] = mfma8_group(bf, af[i]);
+            if (j > 0) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const v4f p = mfma8_group(bf[j], af);
+                for (int i = 0; i < MI; i++) {
+                    if (KIND == 0)
+                        acc[i][j - 1] += pp[i] * c[i];
+                    else
+                        acc[i][j - 1] += (pp[i] * c[i]) * sbp;
+                }
+            }
+            if (KIND == 1) sbp = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
+#pragma unroll
+            for (int i = 0; i < MI; i++) pp[i] = pc[i];
+            if (j + 1 < NJ) bf = bn;
+        }
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
             if (KIND == 0)
-                acc[i][j] += p * c;
+                acc[i][NJ - 1] += pp[i] * c[i];
             else
-                acc[i][j] += (p * c) * sbn[j];
+                acc[i][NJ - 1] += (pp[i] * c[i]) * sbp;
+        }
+    } else {
+        v8i bf[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) bf[j] = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+        v4f sbn[NJ];
+        if (KIND == 1) {
+#pragma unroll
+            for (int j = 0; j < NJ; j++) sbn[j] = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
+        }
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+            if (mbase + 16 * i >= m_valid) break;  // wave-uniform
+            const int mrow = mbase + 16 * i + (lane & 15);
+            const v8i af = f8_frag(la, mrow, c0);
+            const float sam = lsa[mrow];
+            const float c = KIND == 0 ? sam * sbk : sam;
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                const v4f p = mfma8_group(bf[j], af);
+                if (KIND == 0)
+                    acc[i][j] += p * c;
+                else
+                    acc[i][j] += (p * c) * sbn[j];
+            }
         }
     }
 }
@@ -483,30 +564,55 @@ __device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) 
 
 template <int SH, int KIND>
 __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
-                                                   v4f (&acc)[4][4]) {
+                                                   v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ]) {
+    constexpr int MI = Sub<SH>::MI, NJ = Sub<SH>::NJ;
     const uint8_t* la = stage + Lds<SH>::A;
     const uint8_t* lb = stage + Lds<SH>::B;
     const float* lsa = (const float*)(stage + Lds<SH>::SA);
     const float* lsb = (const float*)(stage + Lds<SH>::SB);
-    const int mbase = wm * 64, nbase = wn * 64;
+    const int mbase = wm * Shape<SH>::WM, nbase = wn * Shape<SH>::WN;
     const int c0 = 2 * (lane >> 4);
     if (mbase >= m_valid) return;
 
-    v8i bf[4];
-    int sbb[4];
+    if constexpr (MI < NJ) {
+        v8i af[MI];
+        int sab[MI];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+        for (int i = 0; i < MI; i++) {
+            const int mrow = mbase + 16 * i + (lane & 15);
+            af[i] = f8_frag(la, mrow, c0);
+            sab[i] = e8m0(lsa[mrow]);
+        }
+        // B fragment j+1 is read while column j's MFMAs run
+        v8i bf = f8_frag(lb, nbase + (lane & 15), c0);
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            v8i bn;
+            if (j + 1 < NJ) bn = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
+            const int sbb = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], acc[i][j], 0, 0, 0, sbb, 0,
+                                                                             sab[i]);
+            if (j + 1 < NJ) bf = bn;
+        }
+        return;
+    }
+    v8i bf[NJ];
+    int sbb[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
         bf[j] = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
         sbb[j] = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < MI; i++) {
         if (mbase + 16 * i >= m_valid) break;  // wave-uniform
         const int mrow = mbase + 16 * i + (lane & 15);
         const v8i af = f8_frag(la, mrow, c0);
         const int sab = e8m0(lsa[mrow]);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < NJ; j++)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbb[j], 0, sab);
     }
 }
@@ -538,10 +644,11 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
     }
 }
 
-// The tile leaves through LDS: every wave writes its accumulators into a
-// row-major fp32 image of the tile (row stride BN + 4 floats, which spreads
-// consecutive rows over the banks), then each row of the tile is stored with
-// 32 lanes writing 16 contiguous bytes each (fp32) or 8 (bf16).  Written
+// The tile leaves through LDS, 128 columns at a time: the waves holding
+// those columns write their accumulators into a row-major fp32 image (row
+// stride 128 + 4 floats, which spreads consecutive rows over the banks), then
+// each row of the image is stored with 32 lanes writing 16 contiguous bytes
+// each (fp32) or 8 (bf16).  Written
 // straight from the MFMA layout, a store instruction would touch 32 rows with
 // 32 bytes each; through LDS it writes whole 512- or 256-byte row segments,
 // which matters where the output is large next to the work (fp32 gradients
@@ -549,8 +656,10 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
 // loop (wait_and_barrier<0>) before this runs.
 template <int SH>
 struct Epi {
-    static constexpr int LD = Shape<SH>::BN + 4;
-    static_assert(Shape<SH>::BM * LD * 4 <= Lds<SH>::BYTES, "the tile image fits in the stages");
+    static constexpr int W = 128;  // columns per image
+    static constexpr int LD = W + 4;
+    static_assert(Shape<SH>::BM * LD * 4 <= Lds<SH>::BYTES, "the image fits in the stages");
+    static_assert(Shape<SH>::BN % W == 0 && W % Shape<SH>::WN == 0, "waves' columns tile the images");
 };
 
 template <int SH>
@@ -559,16 +668,18 @@ __device__ __forceinline__ void put4(float* ep, int row, int col, float v0, floa
 }
 
 // OUT: 0 bf16, 1 fp32, 2 / 3 the bf16 result quantised in 1x128 groups
-// along n with FP32 / power-of-two scales (the tile's 128 columns are one
-// group of every row), codes to d, scales to T.qs.
+// along n with FP32 / power-of-two scales (the image's 128 columns, starting
+// at output column n0, are one group of every row), codes to d, scales to
+// T.qs.
 template <int SH, int OUT>
-__device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T, void* d, int64_t ldd) {
-    constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
-    constexpr int LPR = BN / 4;               // lanes per row
+__device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T, int64_t n0, void* d,
+                                                 int64_t ldd) {
+    constexpr int BM = Shape<SH>::BM, W = Epi<SH>::W;
+    constexpr int LPR = W / 4;                // lanes per row
     constexpr int RPI = THREADS / LPR;        // rows per pass
     const int t = threadIdx.x;
     const int col = (t % LPR) * 4;
-    const int64_t n = T.n0 + col;
+    const int64_t n = n0 + col;
     if constexpr (OUT <= 1) {
 #pragma unroll 4
         for (int r = t / LPR; r < BM; r += RPI) {
@@ -578,7 +689,7 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
             store4<OUT>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
         }
     } else {
-        static_assert(BN == 128 && LPR == 32, "one 1x128 group per tile row, 32 lanes per row");
+        static_assert(W == 128 && LPR == 32, "one 1x128 group per image row, 32 lanes per row");
         // Every lane runs every pass (the 32-lane reductions need them all);
         // only the stores are masked.
         for (int r = t / LPR; r < BM; r += RPI) {
@@ -592,9 +703,9 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
             const GroupScale gs = group_scale(am, OUT == 3);
             const uint32_t codes = pack4(bf16_lo(b0) * gs.inv, bf16_lo(b1) * gs.inv, bf16_lo(b2) * gs.inv,
                                          bf16_lo(b3) * gs.inv);
-            if (m < T.m_end) {
+            if (m < T.m_end && n < T.n_end) {
                 *(uint32_t*)((uint8_t*)d + m * ldd + n) = codes;
-                if (col == 0) T.qs[(T.n0 >> 7) * T.qlds + m] = gs.s;
+                if (col == 0) T.qs[(n0 >> 7) * T.qlds + m] = gs.s;
             }
         }
     }
@@ -612,24 +723,32 @@ __device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T
             for (int q = 0; q < 4; q++)
                 put4<SH>(ep, wm * 64 + 32 * i + (lane & 31), wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5),
                          acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    static_assert(Shape<SH>::BN == Epi<SH>::W, "one image");
     __syncthreads();
-    write_tile_image<SH, OUT>(ep, T, d, ldd);
+    write_tile_image<SH, OUT>(ep, T, T.n0, d, ldd);
     __syncthreads();  // the stages may be refilled by a following tile
 }
 
 template <int SH, int OUT>
-__device__ __forceinline__ void store_mfma8(const v4f (&acc)[4][4], const Tile& T, int wm, int wn, int lane,
-                                            void* d, int64_t ldd, uint8_t* smem) {
+__device__ __forceinline__ void store_mfma8(const v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ], const Tile& T, int wm,
+                                            int wn, int lane, void* d, int64_t ldd, uint8_t* smem) {
+    constexpr int W = Epi<SH>::W, WM = Shape<SH>::WM, WN = Shape<SH>::WN;
     float* ep = (float*)smem;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int h = 0; h < Shape<SH>::BN / W; h++) {
+        if (T.n0 + h * W >= T.n_end) break;  // workgroup-uniform: columns past the end
+        if (wn * WN / W == h) {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            put4<SH>(ep, wm * 64 + 16 * i + (lane & 15), wn * 64 + 16 * j + 4 * (lane >> 4), acc[i][j][0],
-                     acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-    __syncthreads();
-    write_tile_image<SH, OUT>(ep, T, d, ldd);
-    __syncthreads();
+            for (int i = 0; i < Sub<SH>::MI; i++)
+#pragma unroll
+                for (int j = 0; j < Sub<SH>::NJ; j++)
+                    put4<SH>(ep, wm * WM + 16 * i + (lane & 15), wn * WN % W + 16 * j + 4 * (lane >> 4),
+                             acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+        __syncthreads();
+        write_tile_image<SH, OUT>(ep, T, T.n0 + h * W, d, ldd);
+        __syncthreads();
+    }
 }
 
 // ==== one tile: pipelined K loop, then the store ==============================================
@@ -644,7 +763,10 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     Shape<SH>::wave_grid(wave, wm, wn);
     const int m_valid = (int)(T.m_end - T.m0 < Shape<SH>::BM ? T.m_end - T.m0 : Shape<SH>::BM);
 
-    typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[4][4]>::type AccT;  // ACC 1, 2: 16x16 sub-tiles
+    static_assert(ACC != 0 || SH == 0, "the f16 path runs on 64 x 64 wave tiles");
+    constexpr int MI = Sub<SH>::MI, NJ = Sub<SH>::NJ;
+    // ACC 0: 32x32 sub-tiles; ACC 1, 2: 16x16 sub-tiles
+    typedef typename std::conditional<ACC == 0, v16f[2][2], v4f[MI][NJ]>::type AccT;
     AccT acc;
     if constexpr (ACC == 0) {
 #pragma unroll
@@ -655,9 +777,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
                 for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < MI; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
     // pipelined block-kind f16 path: previous group's partials and factors
@@ -678,16 +800,17 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         if (g0 + s < g1) stg.issue(T, g0 + s, smem, s * Lds<SH>::STAGE, wave);
 
     // Tile loads per group per wave; waves that also load scales issue one
-    // more, so waiting for PER outstanding is conservative for them.
+    // more, so waiting for PER outstanding is conservative for them.  With
+    // two stages the following group is issued only after the wait.
     constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / WAVES;
-    static_assert(S == 3 && PER == 6, "wait counts cover this pipeline");
+    static_assert((S == 3 && PER == 6) || S == 2, "wait counts cover this pipeline");
     // One group: wait until it has landed (at most the following group
     // still in flight) for every wave and every wave is done with the stage
     // of the previous group, refill that stage, compute.  The stage index SS
     // is a compile-time constant, so LDS addresses fold into immediates.
     auto step = [&](auto ss, int64_t g) {
         constexpr int SS = decltype(ss)::value;
-        if (g + 1 < g1)
+        if (S == 3 && g + 1 < g1)
             wait_and_barrier<6>();
         else
             wait_and_barrier<0>();
@@ -699,7 +822,7 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
             compute_f32_tile<SH>(stage, wm, wn, lane, m_valid, acc);
         } else {
             if constexpr (ACC == 1)
-                compute_mfma8<SH, KIND>(stage, T, g, wm, wn, lane, m_valid, acc);
+                compute_mfma8<SH, KIND>(stage, wm, wn, lane, m_valid, acc);
             else
                 compute_mfma8_pow2<SH, KIND>(stage, wm, wn, lane, m_valid, acc);
         }
@@ -707,7 +830,8 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     for (int64_t g = g0; g < g1; g += S) {
         step(std::integral_constant<int, 0>(), g);
         if (g + 1 < g1) step(std::integral_constant<int, 1>(), g + 1);
-        if (g + 2 < g1) step(std::integral_constant<int, 2>(), g + 2);
+        if constexpr (S == 3)
+            if (g + 2 < g1) step(std::integral_constant<int, 2>(), g + 2);
     }
     if constexpr (ACC == 0 && KIND == 0) {
 #pragma unroll
@@ -725,9 +849,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
 
 // ==== kernels ==========================================================================
 
-template <int ACC, int KIND, int OUT, bool SPLIT>
+template <int ACC, int SH, int KIND, int OUT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<SH>::BYTES];
     const int64_t ntiles = tiles_m * tiles_n;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t split = SPLIT ? wid / ntiles : 0;
@@ -735,9 +859,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
     tile_coords(wid % ntiles, tiles_m, tiles_n, tm, tn);
 
     Tile T;
-    T.m0 = tm * Shape<0>::BM;
+    T.m0 = tm * Shape<SH>::BM;
     T.m_end = p.M;
-    T.n0 = tn * Shape<0>::BN;
+    T.n0 = tn * Shape<SH>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -756,8 +880,53 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
         const int64_t per = (groups + p.splits - 1) / p.splits;
         const int64_t g0 = split * per;
         const int64_t g1 = g0 + per < groups ? g0 + per : groups;
-        run_tile<ACC, 0, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
+        run_tile<ACC, SH, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
     } else {
+        run_tile<ACC, SH, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
+    }
+}
+
+// FP8 dense paths: one launch, two tile shapes.  Output columns [0, n1)
+// (n1 a multiple of 256, possibly past N) run on 256 x 256 tiles
+// (workgroups 0 .. wide-1), the rest on 256 x 128
+// tiles (the following workgroups): a last, partial round of wide tiles
+// becomes a full round of narrow ones.  Each region is XCD-remapped on its
+// own, so both spread over all XCDs in dispatch order.
+template <int ACC, int KIND, int OUT>
+__global__ __launch_bounds__(THREADS) void gemm_wide_kernel(GemmArgs p, int64_t n1) {
+    constexpr int LDS_BYTES = Lds<0>::BYTES > Lds<1>::BYTES ? Lds<0>::BYTES : Lds<1>::BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+    static_assert(Shape<0>::BM == Shape<1>::BM, "both regions share the m tiling");
+    const int64_t tiles_m = (p.M + Shape<1>::BM - 1) / Shape<1>::BM;
+    const int64_t wide = tiles_m * (n1 / Shape<1>::BN);
+    Tile T;
+    T.m_end = p.M;
+    T.a = p.a;
+    T.lda = p.lda;
+    T.sa = p.sa;
+    T.ldsa = p.ldsa;
+    T.b = p.b;
+    T.ldb = p.ldb;
+    T.sb = p.sb;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = p.sb_s1;
+    T.qs = p.qs;
+    T.qlds = p.qlds;
+    const int64_t groups = p.K / 128;
+    int64_t tm, tn;
+    if ((int64_t)blockIdx.x < wide) {
+        tile_coords(xcd_remap(blockIdx.x, wide), tiles_m, n1 / Shape<1>::BN, tm, tn);
+        T.m0 = tm * Shape<1>::BM;
+        T.n0 = tn * Shape<1>::BN;
+        T.n_end = n1 < p.N ? n1 : p.N;
+        run_tile<ACC, 1, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
+    } else {
+        // only launched when n1 < N
+        const int64_t tiles_n = (p.N - n1 + Shape<0>::BN - 1) / Shape<0>::BN;
+        tile_coords(xcd_remap(blockIdx.x - wide, gridDim.x - wide), tiles_m, tiles_n, tm, tn);
+        T.m0 = tm * Shape<0>::BM;
+        T.n0 = n1 + tn * Shape<0>::BN;
+        T.n_end = p.N;
         run_tile<ACC, 0, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
@@ -878,22 +1047,72 @@ size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
     return (size_t)s * (size_t)M * (size_t)((N + 3) / 4 * 4) * sizeof(float);
 }
 
-template <int ACC, int KIND, int OUT, bool SPLIT>
-static void launch_dense(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, int64_t wgs, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<ACC, KIND, OUT, SPLIT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g,
+template <int ACC, int SH, int KIND, int OUT, bool SPLIT>
+static void launch_shape(const GemmArgs& g, hipStream_t st) {
+    const int64_t tiles_m = (g.M + Shape<SH>::BM - 1) / Shape<SH>::BM;
+    const int64_t tiles_n = (g.N + Shape<SH>::BN - 1) / Shape<SH>::BN;
+    const int64_t wgs = tiles_m * tiles_n * (SPLIT ? g.splits : 1);
+    hipLaunchKernelGGL((gemm_kernel<ACC, SH, KIND, OUT, SPLIT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g,
                        tiles_m, tiles_n);
+}
+
+// Compute units of the current device (one workgroup of either shape fills
+// a CU's LDS, so this is also the number of tiles in flight).
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// The FP8 paths run the first n1 output columns on 256 x 256 tiles and the
+// rest on 256 x 128 tiles.  n1 (a multiple of 256; n1 >= N puts every
+// column on wide tiles) minimises the rounds of
+// workgroups, counting a round of the narrow tiles as 0.65 of a round of
+// the wide ones (their measured time per tile): 4096 x 18432, 4.5 rounds
+// of wide tiles, becomes 4 rounds of wide tiles and one of narrow ones.
+int64_t wide_columns(int64_t M, int64_t N, int cus) {
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    int64_t best_n1 = 256 * tn;  // every column on wide tiles
+    double best = (double)((tm * tn + cus - 1) / cus);
+    for (int64_t n1t = 0; n1t < tn; n1t++) {
+        const int64_t t1 = tm * n1t, t0 = tm * ((N - 256 * n1t + 127) / 128);
+        const double cost = (double)((t1 + cus - 1) / cus) + 0.65 * (double)((t0 + cus - 1) / cus);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_n1 = 256 * n1t;
+        }
+    }
+    return best_n1;
+}
+
+// Split-K and the f16 path use shape 0; the FP8 paths gemm_wide_kernel,
+// shape 1 on the first wide_columns() columns and shape 0 on the rest.
+template <int ACC, int KIND, int OUT, bool SPLIT>
+static void launch_dense(const GemmArgs& g, hipStream_t st) {
+    if constexpr (ACC == 0 || SPLIT) {
+        launch_shape<ACC, 0, KIND, OUT, SPLIT>(g, st);
+    } else {
+        const int64_t n1 = wide_columns(g.M, g.N, device_cus());
+        const int64_t tiles_m = (g.M + Shape<1>::BM - 1) / Shape<1>::BM;
+        const int64_t narrow_n = n1 < g.N ? (g.N - n1 + Shape<0>::BN - 1) / Shape<0>::BN : 0;
+        const int64_t wgs = tiles_m * (n1 / Shape<1>::BN) + tiles_m * narrow_n;
+        hipLaunchKernelGGL((gemm_wide_kernel<ACC, KIND, OUT>), dim3((unsigned)wgs), dim3(THREADS), 0, st, g, n1);
+    }
 }
 
 template <int ACC>
 static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
-    const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
-    const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     if (g.splits > 1 && !g.out_quant) {
-        const int64_t wgs = tiles_m * tiles_n * g.splits;
         if (g.bscale_kind == 0)
-            launch_dense<ACC, 0, 1, true>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 0, 1, true>(g, st);
         else
-            launch_dense<ACC, 1, 1, true>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 1, 1, true>(g, st);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = g.M * ((g.N + 3) / 4);
@@ -906,31 +1125,30 @@ static hipError_t launch_gemm_acc(const GemmArgs& g, hipStream_t st) {
                                g.d, g.ldd);
         return hipGetLastError();
     }
-    const int64_t wgs = tiles_m * tiles_n;
     if (g.out_quant) {
         if (g.bscale_kind == 0) {
             if (g.out_quant == 1)
-                launch_dense<ACC, 0, 2, false>(g, tiles_m, tiles_n, wgs, st);
+                launch_dense<ACC, 0, 2, false>(g, st);
             else
-                launch_dense<ACC, 0, 3, false>(g, tiles_m, tiles_n, wgs, st);
+                launch_dense<ACC, 0, 3, false>(g, st);
         } else {
             if (g.out_quant == 1)
-                launch_dense<ACC, 1, 2, false>(g, tiles_m, tiles_n, wgs, st);
+                launch_dense<ACC, 1, 2, false>(g, st);
             else
-                launch_dense<ACC, 1, 3, false>(g, tiles_m, tiles_n, wgs, st);
+                launch_dense<ACC, 1, 3, false>(g, st);
         }
         return hipGetLastError();
     }
     if (g.bscale_kind == 0) {
         if (g.out_f32)
-            launch_dense<ACC, 0, 1, false>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 0, 1, false>(g, st);
         else
-            launch_dense<ACC, 0, 0, false>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 0, 0, false>(g, st);
     } else {
         if (g.out_f32)
-            launch_dense<ACC, 1, 1, false>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 1, 1, false>(g, st);
         else
-            launch_dense<ACC, 1, 0, false>(g, tiles_m, tiles_n, wgs, st);
+            launch_dense<ACC, 1, 0, false>(g, st);
     }
     return hipGetLastError();
 }

@@ -57,7 +57,8 @@ struct GemmArgs {
     int out_quant;
     float* qs;
     int64_t qlds;
-    int accum;    // 0 FP32-accurate group partials (f16 matrix cores), 1 FP8 matrix cores
+    int accum;    // 0 FP32-accurate group partials (f16 matrix cores), 1 FP8 matrix cores,
+                  // 2 FP8 matrix cores with the power-of-two scales inside the MFMA
     // split-K (dense only): partials in `ws`, row stride ws_ld floats
     float* ws;
     int splits;
@@ -73,6 +74,9 @@ struct GemmArgs {
 int gemm_splits(int64_t M, int64_t N, int64_t K);
 // Workspace bytes the dense GEMM needs for this shape.
 size_t gemm_workspace(int64_t M, int64_t N, int64_t K);
+// Output columns the FP8 dense paths run on 256 x 256 tiles (the rest on
+// 256 x 128 tiles), given the device's compute units.
+int64_t wide_columns(int64_t M, int64_t N, int cus);
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);
