@@ -20,8 +20,10 @@
 //
 //  ACC_MFMA8 (1).  P_g straight from v_mfma_f32_16x16x128_f8f6f4 (one MFMA
 //  is one K group of a 16x16 sub-tile) at twice the matrix-core rate, with
-//  the matrix core's own limited accumulation inside the group.  Workgroup
-//  tile 256 (m) x 128 (n); 8 waves of 64x64, 4x4 sub-tiles of 16x16.
+//  the matrix core's own limited accumulation inside the group.  Dense
+//  launches: workgroup tile 256 (m) x 256 (n), 8 waves of 64x128 (4x8
+//  sub-tiles of 16x16), the last partial round of tiles as 256 x 128 tiles
+//  (waves of 64x64); split-K and grouped launches: 256 x 128.
 //
 //  ACC_MFMA8_POW2 (2).  As ACC_MFMA8, for power-of-two scales: they enter
 //  the scaled MFMA as E8M0 block scales and every group is accumulated by
@@ -41,7 +43,7 @@
 // global_load_lds (see dma16s, Stager).  Tiles sit in LDS as FP8 codes,
 // rows of 128 B whose 16-byte chunks are XOR-swizzled by (row & 7) ^ (row>>3 & 1)
 // -- lanes fetch the permuted chunk of their row, so coalescing is unchanged
-// and the fragment reads of 8 or 16 consecutive rows hit distinct banks.
+// and the fragment reads of 16 consecutive rows spread over all banks.
 // STAGES groups are in flight; one barrier per group both publishes the
 // landed group and frees the stage the next issue overwrites.
 //
@@ -488,40 +490,19 @@ __device__ __forceinline__ void compute_mfma8(const uint8_t* stage, int wm, int 
             af[i] = f8_frag(la, mrow, c0);
             c[i] = KIND == 0 ? lsa[mrow] * sbk : lsa[mrow];
         }
-        // Software-pipelined over the B fragments: fragment j+1 is read
-        // while column j's MFMAs run, and column j's partials are promoted
-        // after column j+1's MFMAs are issued, so neither the LDS latency
-        // nor the MFMA latency stalls the wave.
-        v8i bf = f8_frag(lb, nbase + (lane & 15), c0);
-        v4f pp[MI];
-        v4f sbp;
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
-            v8i bn;
-            if (j + 1 < NJ) bn = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
-            v4f pc[MI];
+            const v8i bf = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+            v4f sbn;
+            if (KIND == 1) sbn = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
 #pragma unroll
-            for (int i = 0; i < MI; i++) pc[i] = mfma8_group(bf, af[i]);
-            if (j > 0) {
-#pragma unroll
-                for (int i = 0; i < MI; i++) {
-                    if (KIND == 0)
-                        acc[i][j - 1] += pp[i] * c[i];
-                    else
-                        acc[i][j - 1] += (pp[i] * c[i]) * sbp;
-                }
+            for (int i = 0; i < MI; i++) {
+                const v4f p = mfma8_group(bf, af[i]);
+                if (KIND == 0)
+                    acc[i][j] += p * c[i];
+                else
+                    acc[i][j] += (p * c[i]) * sbn;
             }
-            if (KIND == 1) sbp = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
-#pragma unroll
-            for (int i = 0; i < MI; i++) pp[i] = pc[i];
-            if (j + 1 < NJ) bf = bn;
-        }
-#pragma unroll
-        for (int i = 0; i < MI; i++) {
-            if (KIND == 0)
-                acc[i][NJ - 1] += pp[i] * c[i];
-            else
-                acc[i][NJ - 1] += (pp[i] * c[i]) * sbp;
         }
     } else {
         v8i bf[NJ];
@@ -583,18 +564,14 @@ __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm,
             af[i] = f8_frag(la, mrow, c0);
             sab[i] = e8m0(lsa[mrow]);
         }
-        // B fragment j+1 is read while column j's MFMAs run
-        v8i bf = f8_frag(lb, nbase + (lane & 15), c0);
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
-            v8i bn;
-            if (j + 1 < NJ) bn = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
+            const v8i bf = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
             const int sbb = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
 #pragma unroll
             for (int i = 0; i < MI; i++)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], acc[i][j], 0, 0, 0, sbb, 0,
                                                                              sab[i]);
-            if (j + 1 < NJ) bf = bn;
         }
         return;
     }
