@@ -956,21 +956,26 @@ __device__ __forceinline__ int64_t expert_first_group(const int32_t* __restrict_
     return total;
 }
 
+// Each workgroup takes a strip of KSTRIP n-tiles of one (expert, m-tile):
+// experts hold few tokens, so a tile's K loop is short and the expert's
+// group range (two dependent reads of the offsets) is looked up once per
+// strip rather than once per tile.
+constexpr int KSTRIP = 8;
+
 template <int ACC, int OUT>
 __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
-    const int64_t per = tiles_m * tiles_n;
+    const int64_t strips = (tiles_n + KSTRIP - 1) / KSTRIP;
+    const int64_t per = tiles_m * strips;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t e = wid / per;
-    int64_t tm, tn;
-    tile_coords(wid % per, tiles_m, tiles_n, tm, tn);
+    const int64_t tm = (wid % per) % tiles_m, strip = (wid % per) / tiles_m;
     const int64_t g0 = expert_first_group(p.offsets, e);
     const int64_t g1 = g0 + ((int64_t)p.offsets[e + 1] - p.offsets[e] + 127) / 128;
 
     Tile T;
     T.m0 = tm * Shape<0>::BM;
     T.m_end = p.M;
-    T.n0 = tn * Shape<0>::BN;
     T.n_end = p.N;
     T.a = p.a;
     T.lda = p.lda;
@@ -982,7 +987,11 @@ __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t t
     T.sb_s0 = p.sb_s0;
     T.sb_s1 = 0;
     void* d = (uint8_t*)p.d + e * p.d_estride * (OUT ? 4 : 2);
-    run_tile<ACC, 0, 1, OUT>(T, g0, g1, d, p.ldd, smem);
+    const int64_t tn_end = (strip + 1) * KSTRIP < tiles_n ? (strip + 1) * KSTRIP : tiles_n;
+    for (int64_t tn = strip * KSTRIP; tn < tn_end; tn++) {
+        T.n0 = tn * Shape<0>::BN;
+        run_tile<ACC, 0, 1, OUT>(T, g0, g1, d, p.ldd, smem);
+    }
 }
 
 // Sum split-K partials in split order and convert.
@@ -1158,7 +1167,7 @@ template <int ACC>
 static hipError_t launch_kgrouped_acc(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
     const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n * g.G));
+    const dim3 grid((unsigned)(tiles_m * ((tiles_n + KSTRIP - 1) / KSTRIP) * g.G));
     if (g.out_f32)
         hipLaunchKernelGGL((kgrouped_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
     else
