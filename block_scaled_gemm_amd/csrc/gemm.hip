@@ -597,6 +597,19 @@ __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm,
 // ==== epilogue ===========================================================================
 
 // Store four consecutive columns n..n+3 of row m (masked at the edges).
+// Four consecutive columns n..n+3 of row m, all inside the output.
+template <int OUT>
+__device__ __forceinline__ void store4_full(void* d, int64_t ldd, int64_t m, int64_t n, float v0, float v1,
+                                            float v2, float v3) {
+    if (OUT) {
+        *(float4*)((float*)d + m * ldd + n) = make_float4(v0, v1, v2, v3);
+    } else {
+        const uint32_t b0 = f32_to_bf16_bits(v0), b1 = f32_to_bf16_bits(v1);
+        const uint32_t b2 = f32_to_bf16_bits(v2), b3 = f32_to_bf16_bits(v3);
+        *(uint2*)((uint16_t*)d + m * ldd + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+}
+
 template <int OUT>
 __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t n, int64_t n_end, float v0,
                                        float v1, float v2, float v3) {
@@ -658,12 +671,24 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
     const int col = (t % LPR) * 4;
     const int64_t n = n0 + col;
     if constexpr (OUT <= 1) {
+        // Images whose columns all lie inside the output store whole
+        // 16- / 8-byte runs with no per-lane edge test (kept apart so the
+        // compiler does not fold the edge path's element stores into them).
+        if (n0 + W <= T.n_end) {
 #pragma unroll 4
-        for (int r = t / LPR; r < BM; r += RPI) {
-            const int64_t m = T.m0 + r;
-            if (m >= T.m_end || n >= T.n_end) continue;
-            const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
-            store4<OUT>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
+            for (int r = t / LPR; r < BM; r += RPI) {
+                const int64_t m = T.m0 + r;
+                if (m >= T.m_end) break;
+                const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
+                store4_full<OUT>(d, ldd, m, n, v.x, v.y, v.z, v.w);
+            }
+        } else {
+            for (int r = t / LPR; r < BM; r += RPI) {
+                const int64_t m = T.m0 + r;
+                if (m >= T.m_end || n >= T.n_end) continue;
+                const float4 v = *(const float4*)&ep[r * Epi<SH>::LD + col];
+                store4<OUT>(d, ldd, m, n, T.n_end, v.x, v.y, v.z, v.w);
+            }
         }
     } else {
         static_assert(W == 128 && LPR == 32, "one 1x128 group per image row, 32 lanes per row");
@@ -1011,7 +1036,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         s.z += v.z;
         s.w += v.w;
     }
-    store4<OUT>(d, ldd, m, n, N, s.x, s.y, s.z, s.w);
+    if (n + 4 <= N)
+        store4_full<OUT>(d, ldd, m, n, s.x, s.y, s.z, s.w);
+    else
+        store4<OUT>(d, ldd, m, n, N, s.x, s.y, s.z, s.w);
 }
 
 // ==== host side ==========================================================================
