@@ -65,6 +65,12 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int THREADS = 512;
 constexpr int WAVES = THREADS / 64;
+// Waves 0..3 (one per SIMD) stage the tiles; waves 4..7 write the output.
+// All eight compute.  A wave's vmcnt counts its loads and its stores
+// alike, so with the roles apart the loaders' waits for the next groups
+// never wait for the previous tile's output stores.
+constexpr int LOADERS = 4;
+constexpr int STORE_THREADS = THREADS - LOADERS * 64;
 
 // Workgroup tile shapes, 8 waves each on a 4 (m) x 2 (n) wave grid.
 //  Shape 0: 256 (m) x 128 (n), waves of 64 x 64, three K groups in flight.
@@ -138,18 +144,15 @@ __device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t 
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
-// Wait until at most N of this wave's direct loads are in flight, then
-// barrier.  The memory clobber keeps the compiler from moving LDS accesses
-// across it.
+// Loader waves wait until at most N of their direct loads are in flight;
+// then every wave meets at the barrier.  The memory clobber keeps the
+// compiler from moving LDS accesses across it.  `wave` is wave-uniform.
 template <int N>
-__device__ __forceinline__ void wait_and_barrier();
-template <>
-__device__ __forceinline__ void wait_and_barrier<0>() {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-}
-template <>
-__device__ __forceinline__ void wait_and_barrier<6>() {
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void wait_and_barrier(int wave) {
+    if (wave < LOADERS)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    else
+        asm volatile("s_barrier" ::: "memory");
 }
 
 // Chunk swizzle of a tile row: (row mod 8) ^ bit 3 of the row.  The 16
@@ -204,69 +207,65 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
 // clamped to the last row, so every load stays inside the operand); per
 // group only the wave-uniform base pointers advance.  Each wave instruction
 // moves 8 rows of 128 B: lane i fetches chunk (i%8) ^ swz(row) of row i/8
-// and lands at LDS base + 16*i.
+// and lands at LDS base + 16*i.  Only the LOADERS waves issue.
 
 template <int SH, int KIND>
 struct Stager {
     static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
-    static constexpr int NA = BM / 8 / WAVES, NB = BN / 8 / WAVES;
-    static constexpr int SA_INS = BM / 64, SB_INS = BN / 64;
-    uint32_t va[NA], vb[NB], vs;
+    static constexpr int NA = BM / 8 / LOADERS, NB = BN / 8 / LOADERS;
+    static constexpr int SA_INS = BM / 64, SB_INS = KIND == 1 ? BN / 64 : 1;
+    static_assert(SA_INS <= LOADERS && SB_INS <= LOADERS, "one instruction per loader for each scale");
+    static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
+    uint32_t va[NA], vb[NB], vsa, vsb;
 
     __device__ __forceinline__ void init(const Tile& T, int wave, int lane) {
 #pragma unroll
         for (int ins = 0; ins < NA; ins++) {
-            const int row = (ins * WAVES + wave) * 8 + (lane >> 3);
+            const int row = (ins * LOADERS + wave) * 8 + (lane >> 3);
             const int64_t m = T.m0 + row < T.m_end ? T.m0 + row : T.m_end - 1;
             va[ins] = (uint32_t)((m - T.m0) * T.lda) + ((((lane & 7) ^ swz(row))) << 4);
         }
 #pragma unroll
         for (int ins = 0; ins < NB; ins++) {
-            const int row = (ins * WAVES + wave) * 8 + (lane >> 3);
+            const int row = (ins * LOADERS + wave) * 8 + (lane >> 3);
             const int64_t n = T.n0 + row < T.n_end ? T.n0 + row : T.n_end - 1;
             vb[ins] = (uint32_t)((n - T.n0) * T.ldb) + ((((lane & 7) ^ swz(row))) << 4);
         }
-        vs = 0;
-        if (wave < SA_INS) {
-            const int64_t m = T.m0 + wave * 64 + lane < T.m_end ? T.m0 + wave * 64 + lane : T.m_end - 1;
-            vs = (uint32_t)(m - T.m0) * 4;
-        } else if (KIND == 1 && wave < SA_INS + SB_INS) {
-            const int w = wave - SA_INS;
-            const int64_t n = T.n0 + w * 64 + lane < T.n_end ? T.n0 + w * 64 + lane : T.n_end - 1;
-            vs = (uint32_t)(n - T.n0) * 4;
-        } else if (KIND == 0 && wave == SA_INS) {
+        const int64_t m = T.m0 + wave * 64 + lane < T.m_end ? T.m0 + wave * 64 + lane : T.m_end - 1;
+        vsa = (uint32_t)(m - T.m0) * 4;
+        if (KIND == 1) {
+            const int64_t n = T.n0 + wave * 64 + lane < T.n_end ? T.n0 + wave * 64 + lane : T.n_end - 1;
+            vsb = (uint32_t)(n - T.n0) * 4;
+        } else {
             // lane l loads the scalar of the tile's block column l (clamped
             // to the last block column present)
             const int64_t last = (T.n_end - 1 - T.n0) >> 7;
             const int64_t blk = lane < last ? lane : last;
-            vs = (uint32_t)(blk * T.sb_s0 * 4);
+            vsb = (uint32_t)(blk * T.sb_s0 * 4);
         }
     }
 
     // Group g into the stage at LDS byte offset `stage` of smem.
     __device__ __forceinline__ void issue(const Tile& T, int64_t g, uint8_t* smem, int stage, int wave) const {
+        if (wave >= LOADERS) return;
         const uint8_t* a = T.a + T.m0 * T.lda + g * 128;
         const uint8_t* b = T.b + T.n0 * T.ldb + g * 128;
         const uint32_t base = lds_addr(smem + stage);
 #pragma unroll
         for (int ins = 0; ins < NA; ins++)
-            dma16s(va[ins], a, base + Lds<SH>::A + (ins * WAVES + wave) * 8 * 128);
+            dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
 #pragma unroll
         for (int ins = 0; ins < NB; ins++)
-            dma16s(vb[ins], b, base + Lds<SH>::B + (ins * WAVES + wave) * 8 * 128);
-        // scales: the first waves load sa (64 floats per instruction); the
-        // waves after them load the B scales -- BN per-column floats (tile
-        // kind) or, block kind, the group's BN/128 block scalars (lane l
-        // loads block column l; the copies past them land in unused words)
-        static_assert(SA_INS + (KIND == 1 ? SB_INS : 1) <= WAVES, "one scale instruction per wave");
-        static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
-        if (wave < SA_INS) {
-            dma4s(vs, T.sa + g * T.ldsa + T.m0, base + Lds<SH>::SA + wave * 256);
-        } else if (KIND == 1 && wave < SA_INS + SB_INS) {
-            dma4s(vs, T.sb + g * T.sb_s0 + T.n0, base + Lds<SH>::SB + (wave - SA_INS) * 256);
-        } else if (KIND == 0 && wave == SA_INS) {
-            dma4s(vs, T.sb + (T.n0 >> 7) * T.sb_s0 + g * T.sb_s1, base + Lds<SH>::SB);
-        }
+            dma16s(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
+        // scales: loader w loads sa rows 64w..64w+63 and the B scales --
+        // per-column floats 64w..64w+63 (tile kind) or, block kind (loader
+        // 0), the group's BN/128 block scalars (lane l loads block column
+        // l; the copies past them land in unused words)
+        if (wave < SA_INS) dma4s(vsa, T.sa + g * T.ldsa + T.m0, base + Lds<SH>::SA + wave * 256);
+        if (KIND == 1 && wave < SB_INS)
+            dma4s(vsb, T.sb + g * T.sb_s0 + T.n0, base + Lds<SH>::SB + wave * 256);
+        else if (KIND == 0 && wave == 0)
+            dma4s(vsb, T.sb + (T.n0 >> 7) * T.sb_s0 + g * T.sb_s1, base + Lds<SH>::SB);
     }
 };
 
@@ -666,8 +665,9 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
                                                  int64_t ldd) {
     constexpr int BM = Shape<SH>::BM, W = Epi<SH>::W;
     constexpr int LPR = W / 4;                // lanes per row
-    constexpr int RPI = THREADS / LPR;        // rows per pass
-    const int t = threadIdx.x;
+    constexpr int RPI = STORE_THREADS / LPR;  // rows per pass
+    const int t = (int)threadIdx.x - LOADERS * 64;
+    if (t < 0) return;  // the loader waves do not store
     const int col = (t % LPR) * 4;
     const int64_t n = n0 + col;
     if constexpr (OUT <= 1) {
@@ -801,11 +801,11 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     for (int s = 0; s < S - 1; s++)
         if (g0 + s < g1) stg.issue(T, g0 + s, smem, s * Lds<SH>::STAGE, wave);
 
-    // Tile loads per group per wave; waves that also load scales issue one
-    // more, so waiting for PER outstanding is conservative for them.  With
-    // two stages the following group is issued only after the wait.
-    constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / WAVES;
-    static_assert((S == 3 && PER == 6) || S == 2, "wait counts cover this pipeline");
+    // Tile loads per group per loader wave; the scale loads come on top, so
+    // waiting for PER outstanding is conservative.  With two stages the
+    // following group is issued only after the wait.
+    constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / LOADERS;
+    static_assert((S == 3 && PER == 12) || S == 2, "wait counts cover this pipeline");
     // One group: wait until it has landed (at most the following group
     // still in flight) for every wave and every wave is done with the stage
     // of the previous group, refill that stage, compute.  The stage index SS
@@ -813,9 +813,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     auto step = [&](auto ss, int64_t g) {
         constexpr int SS = decltype(ss)::value;
         if (S == 3 && g + 1 < g1)
-            wait_and_barrier<6>();
+            wait_and_barrier<PER>(wave);
         else
-            wait_and_barrier<0>();
+            wait_and_barrier<0>(wave);
         if (g + S - 1 < g1) stg.issue(T, g + S - 1, smem, ((SS + S - 1) % S) * Lds<SH>::STAGE, wave);
         const uint8_t* stage = smem + SS * Lds<SH>::STAGE;
         if constexpr (ACC == 0 && KIND == 0) {
@@ -841,7 +841,7 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
 #pragma unroll
             for (int j = 0; j < 2; j++) acc[i][j] += pp[i][j] * cp[i];
     }
-    wait_and_barrier<0>();  // the LDS stages may be reused by a following tile
+    wait_and_barrier<0>(wave);  // the LDS stages may be reused by a following tile
 
     if constexpr (ACC == 0)
         store_f32<SH, OUT>(acc, T, wm, wn, lane, d, ldd, smem);
