@@ -582,13 +582,18 @@ __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm,
             sab[i] = e8m0(lsa[mrow]);
         }
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            const v8i bf = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
-            const int sbb = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
+        for (int j = 0; j < NJ; j += 2) {
+            const v8i b0 = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+            const v8i b1 = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
+            const int s0 = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
+            const int s1 = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * (j + 1) + (lane & 15)]);
 #pragma unroll
             for (int i = 0; i < MI; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], acc[i][j], 0, 0, 0, sbb, 0,
-                                                                             sab[i]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[i], acc[i][j], 0, 0, 0, s0, 0, sab[i]);
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+                acc[i][j + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[i], acc[i][j + 1], 0, 0, 0, s1, 0,
+                                                                                 sab[i]);
         }
         return;
     }
