@@ -1,6 +1,6 @@
 """Benchmark of the fine-grained FP8 linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum mfma8|fp32]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--accum mfma8|fp32|mfma8_pow2]
     python bench.py --traffic-probe     # plain copy of known size, for counter scaling
     python bench.py --workload expert_backward|grouped_upproj|decode_grouped
     python bench.py --library-ceiling   # vendor GEMMs on the dense shape, for context
@@ -28,10 +28,13 @@ hot path over that batch, inputs already in HBM:
     Y = X W^T, block-scaled FP8 GEMM with per-128 FP32 promotion, bf16 out.
 The GEMM's accumulation mode is --accum: mfma8 (the default) forms each
 128-element group partial on the FP8 matrix cores and promotes it in FP32
-registers -- the pages' scheme -- and meets the bf16 gate on this workload;
-fp32 forms the partials exactly on the f16 matrix cores.  `gemm_modes`
-reports both, and the power-of-two-scale mode (the same step with
-power-of-two scales, the scales applied inside the FP8 MFMA).
+registers -- the pages' scheme; fp32 forms the partials exactly on the f16
+matrix cores; mfma8_pow2 applies power-of-two scales inside the FP8 MFMA
+(the default of grouped_upproj, whose scales are powers of two).  Every
+mode meets the gate on every workload (the GPU tests compare every output
+of each workload at its real size).  `gemm_modes` reports the dense GEMM
+in all three (the power-of-two mode on power-of-two quantisations of the
+same tensors).
 
 Prints one JSON line.  `value` is the step's GEMM FLOPs over the step time
 (quantisation included); `roofline` covers the dominant kernel (the GEMM),
@@ -208,7 +211,7 @@ def other_workload(name, args):
     from block_scaled_gemm_amd import inputs
     dev = torch.device("cuda:0")
     to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8}[args.accum]
+    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8, "mfma8_pow2": bs.ACCUM_MFMA8_POW2}[args.accum]
     kernels = []  # (name, fn, work, unit)
     if name == "expert_backward":
         d = inputs.expert_backward()
@@ -334,10 +337,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--accum", choices=["mfma8", "fp32"], default=None,
-                    help="GEMM accumulation: FP8 matrix cores (mfma8) or exact group partials (fp32); "
-                         "default: mfma8 for dense_fprop, fp32 elsewhere (the fastest mode that meets the "
-                         "output's gate on that workload)")
+    ap.add_argument("--accum", choices=["mfma8", "fp32", "mfma8_pow2"], default=None,
+                    help="GEMM accumulation: FP8 matrix cores (mfma8), exact group partials (fp32), or "
+                         "power-of-two scales inside the FP8 MFMA (mfma8_pow2; power-of-two scales only); "
+                         "default: mfma8_pow2 for grouped_upproj, mfma8 elsewhere")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only a plain copy of known size (counter scaling)")
     ap.add_argument("--library-ceiling", action="store_true",
@@ -346,7 +349,17 @@ def main():
                     choices=["dense_fprop", "expert_backward", "grouped_upproj", "decode_grouped", "moe_backward"])
     args = ap.parse_args()
     if args.accum is None:
-        args.accum = "mfma8" if args.workload == "dense_fprop" else "fp32"
+        # the pages' scheme; grouped_upproj quantises with power-of-two
+        # scales, which the scaled MFMA applies itself
+        args.accum = "mfma8_pow2" if args.workload == "grouped_upproj" else "mfma8"
+    if args.workload == "dense_fprop" and args.accum == "mfma8_pow2":
+        print("bench.py: the dense Fprop quantises with FP32 scales; it reports the power-of-two mode "
+              "under gemm_modes", file=sys.stderr)
+        sys.exit(2)
+    if args.accum == "mfma8_pow2" and args.workload not in ("grouped_upproj",):
+        print("bench.py: mfma8_pow2 needs power-of-two scales; only grouped_upproj quantises with them",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fine-grained FP8 linear here is a "
               "single-GPU build (no collectives); run with --gpus 1", file=sys.stderr)
@@ -365,7 +378,7 @@ def main():
     import torch
     import block_scaled_gemm_amd as bs
     from block_scaled_gemm_amd import inputs
-    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8}[args.accum]
+    accum = {"fp32": bs.ACCUM_FP32, "mfma8": bs.ACCUM_MFMA8, "mfma8_pow2": bs.ACCUM_MFMA8_POW2}[args.accum]
     other = "mfma8" if args.accum == "fp32" else "fp32"
     kernel = GEMM_KERNEL[args.accum]
 
