@@ -128,6 +128,35 @@ def test_linear_three_gemms_ragged(hip, orc, mode, out, accum):
     check(out_f64(dw), r, rabs, out, accum, 3, f"ragged wgrad mode={mode} out={out} accum={accum}")
 
 
+@pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
+@pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
+def test_wide_tiles_ragged(hip, orc, mode, out, accum):
+    """The FP8 modes' 256 x 256 tiles with ragged edges (shapes with enough
+    tiles that the launch picks them on a 256-CU MI355X): Fprop X[8155x1024]
+    W[2008x1024], every tile wide, the last row and column of tiles partial;
+    Fprop X[4059x512] W[4196x512], wide tiles up to column 4096 and 256 x 128
+    tiles after it; Wgrad over 512 tokens into 8152 x 2008 (per-column
+    scales on wide tiles).  Every output compared."""
+    if accum == 2 and mode == 0:
+        pytest.skip("the scaled-MFMA mode takes power-of-two scales only")
+    for i, (m, n, k) in enumerate([(8155, 2008, 1024), (4059, 4196, 512)]):
+        X = inputs.random_bf16(131 + 2 * i, (m, k))
+        W = inputs.random_bf16(132 + 2 * i, (n, k), sd=0.02, outliers=False)
+        qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, X, "row", mode)
+        qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, W, "block", mode)
+        y = hip.linear_fprop(qx, sx, qw, sw, out, accum=accum)
+        r, rabs = full(orc, wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
+        check(out_f64(y), r, rabs, out, accum, k // 128, f"wide fprop {m}x{n}x{k} mode={mode} out={out} accum={accum}")
+    dY = inputs.random_bf16(135, (512, 8152), sd=1e-3)
+    X2 = inputs.random_bf16(136, (512, 2008))
+    qdt, sdt, _, wqdt, wsdt, _ = quant_both(hip, orc, dY, "col", mode)
+    qxt, sxt, _, wqxt, wsxt, _ = quant_both(hip, orc, X2, "col", mode)
+    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, out, accum=accum)
+    r, rabs = full(orc, wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
+    check(out_f64(dw), r, rabs, out, accum, 4, f"wide wgrad 8152x2008x512 mode={mode} out={out} accum={accum}")
+
+
 @ACCUMS_POW2
 def test_exact_special_cases(hip, orc, accum):
     """Bit-exact GPU results where the arithmetic is exact: A = identity with
