@@ -105,6 +105,22 @@ struct Shape<1> {
     static constexpr int STAGES = 2;
     __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<0>::wave_grid(wave, wm, wn); }
 };
+//  Shape 2: 128 x 128, waves of 64 x 32, three K groups in flight (four
+//    stages).  The grouped kernels' FP8 paths run row tiles of at most 128
+//    rows (a typical expert) with it: every wave computes, and the stage
+//    holds no rows past the expert, where the 256-row tile idles half its
+//    waves and stages twice the activation bytes.
+template <>
+struct Shape<2> {
+    static constexpr int BM = 128, BN = 128;
+    static constexpr int WM = 64, WN = 32;
+    static constexpr int STAGES = 4;
+    // SIMD s holds waves s and s + 4, one from each m-slot.
+    __device__ static void wave_grid(int wave, int& wm, int& wn) {
+        wm = wave >> 2;
+        wn = wave & 3;
+    }
+};
 
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
@@ -825,17 +841,20 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
         if (g0 + s < g1) stg.issue(T, g0 + s, smem, s * Lds<SH>::STAGE, wave);
 
     // Tile loads per group per loader wave; the scale loads come on top, so
-    // waiting for PER outstanding is conservative.  With two stages the
-    // following group is issued only after the wait.
+    // waiting for k * PER outstanding (k groups issued after this one) is
+    // conservative.  With two stages the following group is issued only
+    // after the wait.
     constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / LOADERS;
-    static_assert((S == 3 && PER == 12) || S == 2, "wait counts cover this pipeline");
-    // One group: wait until it has landed (at most the following group
-    // still in flight) for every wave and every wave is done with the stage
+    static_assert((S == 4 && PER == 8) || (S == 3 && PER == 12) || S == 2, "wait counts cover this pipeline");
+    // One group: wait until it has landed (at most the S - 2 following
+    // groups still in flight) for every wave and every wave is done with the stage
     // of the previous group, refill that stage, compute.  The stage index SS
     // is a compile-time constant, so LDS addresses fold into immediates.
     auto step = [&](auto ss, int64_t g) {
         constexpr int SS = decltype(ss)::value;
-        if (S == 3 && g + 1 < g1)
+        if (S == 4 && g + 2 < g1)
+            wait_and_barrier<2 * PER>(wave);
+        else if (S >= 3 && g + 1 < g1)
             wait_and_barrier<PER>(wave);
         else
             wait_and_barrier<0>(wave);
@@ -855,8 +874,10 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     for (int64_t g = g0; g < g1; g += S) {
         step(std::integral_constant<int, 0>(), g);
         if (g + 1 < g1) step(std::integral_constant<int, 1>(), g + 1);
-        if constexpr (S == 3)
+        if constexpr (S >= 3)
             if (g + 2 < g1) step(std::integral_constant<int, 2>(), g + 2);
+        if constexpr (S == 4)
+            if (g + 3 < g1) step(std::integral_constant<int, 3>(), g + 3);
     }
     if constexpr (ACC == 0 && KIND == 0) {
 #pragma unroll
@@ -978,8 +999,15 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     T.sb = p.sb + e * p.sb_estride;
     T.sb_s0 = p.sb_s0;
     T.sb_s1 = p.sb_s1;
+    static_assert(Lds<2>::BYTES <= Lds<0>::BYTES, "both row-tile shapes fit the LDS");
     for (int64_t m0 = r0; m0 < r1; m0 += Shape<0>::BM) {
         T.m0 = m0;
+        if constexpr (ACC != 0) {
+            if (r1 - m0 <= Shape<2>::BM) {
+                run_tile<ACC, 2, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
+                continue;
+            }
+        }
         run_tile<ACC, 0, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
     }
 }

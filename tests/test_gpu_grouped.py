@@ -70,7 +70,26 @@ def test_grouped_small_with_empty_experts(hip, orc, out, accum):
             check(out_f64(y)[r0:r1], r[r0:r1], rabs[r0:r1], out, accum, 4, f"expert {e} out={out} accum={accum}")
 
 
-def test_grouped_rows_beyond_offsets_untouched(hip, orc):
+@pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_grouped_short_k(hip, orc, K, accum):
+    """Fewer K groups than the row tiles' pipeline depth (1, 2, 3 and 5
+    groups): experts of 128, 64, 0, 17 and 129 rows (full, partial and empty
+    128-row tiles, one just past them), N = 384, fp32 out."""
+    counts = [128, 64, 0, 17, 129]
+    offsets = np.zeros(len(counts) + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    Xcat = inputs.random_bf16(205 + K, (int(offsets[-1]), K))
+    W = inputs.random_bf16(206 + K, (len(counts), 384, K), sd=0.02, outliers=False)
+    qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 1, accum=accum)
+    r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
+    rabs = orc.grouped_gemm(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw)
+    check(out_f64(y), r, rabs, 1, accum, K // 128, f"short K={K} accum={accum}")
+
+
+@pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
+def test_grouped_rows_beyond_offsets_untouched(hip, orc, accum):
     """Rows past offsets[G] (rows_bound larger than the routed rows) are not
     written."""
     offsets = np.array([0, 100, 160], np.int32)
@@ -78,7 +97,7 @@ def test_grouped_rows_beyond_offsets_untouched(hip, orc):
     W = inputs.random_bf16(204, (2, 128, 256), sd=0.02, outliers=False)
     qx, sx, qw, sw, *_ = quant_experts(hip, orc, Xcat, W, 0)
     d = torch.full((200, 128), 3.0, dtype=torch.float32, device="cuda")
-    hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 1, rows_bound=200, d=d)
+    hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 1, rows_bound=200, d=d, accum=accum)
     assert torch.all(d[160:] == 3.0).item()
 
 
