@@ -183,8 +183,13 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
                                                         float* __restrict__ s, int64_t lds,
                                                         int64_t col_tiles) {
     __shared__ uint32_t tile[64 * 64];
-    const int64_t g = blockIdx.x / col_tiles;
-    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
+    // Consecutive workgroups take consecutive row groups of one column tile,
+    // so the transposed code runs they write continue one another in each
+    // output row (14% faster than walking the column tiles of a row group
+    // first, on X[8192 x 7168]).
+    const int64_t gt = gridDim.x / col_tiles;
+    const int64_t g = blockIdx.x % gt;
+    const int64_t c0 = (blockIdx.x / gt) * 64;
     col_group_tile<POW2>(x + g * 128 * ldx, 128, cols, ldx, c0, q + g * 128, ldq, s + g * lds, tile);
 }
 
@@ -244,8 +249,11 @@ __global__ __launch_bounds__(256) void quant_grouped_col_kernel(const uint16_t* 
                                                                 float* __restrict__ s, int64_t lds,
                                                                 int64_t col_tiles) {
     __shared__ uint32_t tile[64 * 64];
-    const int64_t p = blockIdx.x / col_tiles;
-    const int64_t c0 = (blockIdx.x % col_tiles) * 64;
+    // consecutive workgroups: consecutive padded groups of one column tile
+    // (as in quant_col_kernel)
+    const int64_t pt = gridDim.x / col_tiles;
+    const int64_t p = blockIdx.x % pt;
+    const int64_t c0 = (blockIdx.x / pt) * 64;
     int e;
     int64_t j;
     find_expert_group(offsets, G, p, e, j);
@@ -435,8 +443,11 @@ __global__ __launch_bounds__(256) void requant_col_kernel(const uint8_t* __restr
                                                           int64_t col_tiles) {
     __shared__ uint2 tile[128 * 16];
     const int t = threadIdx.x;
-    const int64_t g = blockIdx.x / col_tiles;
-    const int64_t c0 = (blockIdx.x % col_tiles) * 128;
+    // consecutive workgroups: consecutive row groups of one column tile (as
+    // in quant_col_kernel)
+    const int64_t gt = gridDim.x / col_tiles;
+    const int64_t g = blockIdx.x % gt;
+    const int64_t c0 = (blockIdx.x / gt) * 128;
     {
         const int rb = t >> 4, cb = t & 15;
         const uint8_t* src = q + (g * 128 + 8 * rb) * ldq + c0 + 8 * cb;
