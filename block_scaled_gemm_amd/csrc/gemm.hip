@@ -23,7 +23,8 @@
 //  the matrix core's own limited accumulation inside the group.  Dense
 //  launches: workgroup tile 256 (m) x 256 (n), 8 waves of 64x128 (4x8
 //  sub-tiles of 16x16), the last partial round of tiles as 256 x 128 tiles
-//  (waves of 64x64); split-K and grouped launches: 256 x 128.
+//  (waves of 64x64); split-K and grouped launches: 256 x 128, and 128 x 128
+//  for a grouped row tile of at most 128 rows.
 //
 //  ACC_MFMA8_POW2 (2).  As ACC_MFMA8, for power-of-two scales: they enter
 //  the scaled MFMA as E8M0 block scales and every group is accumulated by
