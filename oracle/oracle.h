@@ -14,8 +14,7 @@
  *   [why-be-50529]        why-be.why-be.co.kr, as_center post 50529
  * followed by the passage (figure, heading or topic) the statement comes from.
  *
- * Every function reports the readings it takes where the pages are silent;
- * the same readings are listed in the design doc.
+ * Every function states the reading it takes where the pages are silent.
  */
 #ifndef FP8_ORACLE_H
 #define FP8_ORACLE_H
