@@ -1,0 +1,57 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the mode guards, the
+algorithmic byte counts and the traffic summary's source check."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=120)
+
+
+@pytest.mark.parametrize("args", [["--gpus", "2"], ["--gpus", "8", "--steps", "1"]])
+def test_more_than_one_gpu_is_refused(args):
+    r = run_bench(*args)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("args", [["--accum", "mfma8_pow2"],
+                                  ["--workload", "decode_grouped", "--accum", "mfma8_pow2"]])
+def test_power_of_two_mode_needs_power_of_two_scales(args):
+    r = run_bench(*args)
+    assert r.returncode == 2
+    assert "power-of-two" in r.stderr
+
+
+def test_algorithmic_bytes_of_the_quantisers():
+    # 2 B read + 1 B written per element, 4 B per 1x128 group or 128x128 block
+    assert bench.quant_bytes_row(4096, 7168) == 4096 * 7168 * 3 + 4096 * 56 * 4
+    assert round(bench.quant_bytes_row(4096, 7168) / 1e6, 1) == 89.0
+    assert bench.quant_bytes_block(18432, 7168) == 18432 * 7168 * 3 + 144 * 56 * 4
+    assert round(bench.quant_bytes_block(18432, 7168) / 1e6, 1) == 396.4
+    # a ragged last block-row still counts one scale per block
+    assert bench.quant_bytes_block(130, 256) == 130 * 256 * 3 + 2 * 2 * 4
+
+
+def test_traffic_is_used_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
+    kernel = bench.GEMM_KERNEL["mfma8"]
+    good = tmp_path / "traffic.txt"
+    good.write_text(f"# comment: with a colon\nkernel: {kernel}\nsource_hash: {bench.source_hash(bench.KERNEL_SOURCES)}\n"
+                    "bytes_per_launch: 1234\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
+    assert bench.measured_traffic(kernel) == 1234.0
+    assert bench.measured_traffic("some_other_kernel<0>") is None
+    stale = tmp_path / "stale.txt"
+    stale.write_text(f"kernel: {kernel}\nsource_hash: 0000000000000000\nbytes_per_launch: 1234\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
+    assert bench.measured_traffic(kernel) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
+    assert bench.measured_traffic(kernel) is None
