@@ -205,11 +205,11 @@ def test_quant_grouped_col_small(hip, orc, mode):
     np.testing.assert_array_equal(host(s)[:tp // 128], ws)
 
 
-def _moe_wgrad_check(hip, orc, dY, X, offsets, accum, tag, sample=None):
+def _moe_wgrad_check(hip, orc, dY, X, offsets, accum, tag, sample=None, mode=0):
     counts = np.diff(offsets)
-    dw = hip.moe_wgrad(dev(offsets), dev_bf16(dY), dev_bf16(X), 0, out_dtype=1, accum=accum)
-    wqd, wsd = orc.quant_tile_grouped_col(dY, offsets, 0)
-    wqx, wsx = orc.quant_tile_grouped_col(X, offsets, 0)
+    dw = hip.moe_wgrad(dev(offsets), dev_bf16(dY), dev_bf16(X), mode, out_dtype=1, accum=accum)
+    wqd, wsd = orc.quant_tile_grouped_col(dY, offsets, mode)
+    wqx, wsx = orc.quant_tile_grouped_col(X, offsets, mode)
     starts, _ = _padded(counts)
     N, C = dY.shape[1], X.shape[1]
     for e, n in enumerate(counts):
@@ -242,6 +242,19 @@ def test_moe_wgrad_small(hip, orc, accum):
     dY = inputs.random_bf16(222, (int(offsets[-1]), 256), sd=1e-3)
     X = inputs.random_bf16(223, (int(offsets[-1]), 200))
     _moe_wgrad_check(hip, orc, dY, X, offsets, accum, f"moe wgrad small accum={accum}")
+
+
+@ACCUMS_POW2
+def test_moe_wgrad_token_tails(hip, orc, accum):
+    """Experts whose last 128-token group holds 31, 32, 33, 64, 65, 96, 97,
+    128, 1, 63 and 127 tokens (every count of 32-token blocks the FP8 paths
+    stage for it), N = 256, C = 384; power-of-two scales for the mode that
+    needs them."""
+    counts = [31, 32, 33, 64, 65, 96, 97, 128, 129, 191, 255]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dY = inputs.random_bf16(224, (int(offsets[-1]), 256), sd=1e-3)
+    X = inputs.random_bf16(225, (int(offsets[-1]), 384))
+    _moe_wgrad_check(hip, orc, dY, X, offsets, accum, f"moe wgrad tails accum={accum}", mode=int(accum == 2))
 
 
 @ACCUMS
