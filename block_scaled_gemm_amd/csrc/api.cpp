@@ -177,6 +177,7 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
         if (K > 0 && (!a || !sa || !b || !sb)) return FP8BS_ERR_ARG;
     }
     if (K % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (lda > FP8BS_MAX_LD || ldb > FP8BS_MAX_LD) return FP8BS_ERR_SHAPE;  // 32-bit per-lane row offsets
     if (lda < K || ldb < K || ldd < N || ldsa < M) return FP8BS_ERR_ARG;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
         (K > 0 && (lda % 16 != 0 || ldb % 16 != 0)) || ldd % 4 != 0)

@@ -57,11 +57,16 @@ extern "C" {
 
 #define FP8BS_ABI_VERSION 3
 
+/* Largest lda / ldb (bytes) the GEMMs take: the kernels address the rows of
+ * a 256-row tile with 32-bit offsets (255 * 2^24 + 127 < 2^32). */
+#define FP8BS_MAX_LD (1LL << 24)
+
 /* Status codes. */
 enum {
     FP8BS_OK = 0,
     FP8BS_ERR_ARG = 1,       /* null pointer, bad enum, negative size, ld too small */
-    FP8BS_ERR_SHAPE = 2,     /* a grouped dimension is not a multiple of 128 */
+    FP8BS_ERR_SHAPE = 2,     /* a grouped dimension is not a multiple of 128, or a
+                                GEMM code stride is above FP8BS_MAX_LD */
     FP8BS_ERR_ALIGN = 3,     /* pointer or leading dimension misaligned */
     FP8BS_ERR_WORKSPACE = 4, /* workspace missing or too small */
     FP8BS_ERR_DEVICE = 5,    /* current device is not gfx950 / no device */
@@ -292,7 +297,8 @@ int fp8_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
  * Alignment: a, b 16-byte aligned, lda and ldb multiples of 16 (when
  * K > 0); d 16-byte
  * aligned, ldd a multiple of 4 elements; sa, sb 4-byte aligned.
- * lda, ldb >= K; ldd >= N; ldsa >= M.
+ * lda, ldb >= K; ldd >= N; ldsa >= M; lda, ldb <= FP8BS_MAX_LD (every GEMM
+ * call below has the same bound).
  * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP.
  */
 int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t *a,

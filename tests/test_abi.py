@@ -141,6 +141,10 @@ def _gemm(**kw):
     (dict(lda=520), ALIGN), (dict(ldd=258), ALIGN), (dict(sa=FAKE + 1), ALIGN),
     (dict(M=0), OK), (dict(N=0), OK),
     (dict(M=256, N=256, K=65536, lda=65536, ldb=65536), WORKSPACE),
+    # code strides: the kernels' per-lane row offsets inside a tile are 32-bit
+    # (M = 0 stops after the argument checks, before any device work)
+    (dict(lda=(1 << 24) + 16), SHAPE), (dict(ldb=(1 << 24) + 16), SHAPE), (dict(M=0, lda=(1 << 24) + 16), SHAPE),
+    (dict(M=0, lda=1 << 24, ldb=1 << 24), OK),
 ])
 def test_gemm_validation(kw, want):
     assert _gemm(**kw) == want
