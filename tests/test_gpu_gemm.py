@@ -128,6 +128,31 @@ def test_linear_three_gemms_ragged(hip, orc, mode, out, accum):
     check(out_f64(dw), r, rabs, out, accum, 3, f"ragged wgrad mode={mode} out={out} accum={accum}")
 
 
+@ACCUMS_POW2
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
+@pytest.mark.parametrize("shape", [(1, 1, 128), (1, 300, 256), (257, 1, 128), (3, 129, 384), (511, 257, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_degenerate_shapes(hip, orc, shape, mode, accum):
+    """Fprop at the smallest and most ragged sizes: a single row, a single
+    column, a single K group, tiles holding 1-3 rows or columns; bf16 and
+    fp32 out into padded outputs (their row stride a multiple of 4)."""
+    if accum == 2 and mode == 0:
+        pytest.skip("the scaled-MFMA mode takes power-of-two scales only")
+    M, N, K = shape
+    X = inputs.random_bf16(140 + M, (M, K))
+    W = inputs.random_bf16(141 + N, (N, K), sd=0.02, outliers=False)
+    qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, X, "row", mode)
+    qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, W, "block", mode)
+    r, rabs = full(orc, wqx, wsx, wqw, wsw, 0, wsw.shape[1], 1)
+    npad = (N + 3) // 4 * 4
+    for out in (1, 0):
+        dt = torch.float32 if out else torch.bfloat16
+        dpad = torch.full((M, npad), 7.0, dtype=dt, device="cuda")
+        hip.fp8_gemm_blockscaled(qx, sx, qw, sw, hip.BSCALE_BLOCK, sw.stride(0), 1, out, d=dpad[:, :N], accum=accum)
+        check(out_f64(dpad[:, :N]), r, rabs, out, accum, K // 128, f"{M}x{N}x{K} mode={mode} out={out} accum={accum}")
+        assert torch.all(dpad[:, N:] == 7.0).item(), "columns past N written"
+
+
 @pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
