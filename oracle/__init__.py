@@ -40,6 +40,12 @@ def _check(rc, what):
         raise ValueError(f"oracle {what} failed with code {rc}")
 
 
+def _check_positive(s, name):
+    s = np.asarray(s)
+    if s.size and not np.all(s > 0):
+        raise ValueError(f"{name}: scales must be positive")
+
+
 def _declare(L):
     L.orc_e4m3_encode.restype = ctypes.c_uint8
     L.orc_e4m3_encode.argtypes = [ctypes.c_float]
@@ -78,6 +84,11 @@ def _declare(L):
     L.orc_grouped_gemm_entries.argtypes = [ctypes.c_int, _i64, _i64, _i32p,
                                            _u8p, _i64, _f32p, _i64, _u8p,
                                            _f32p, _i64, _i64p, _i64p, _f64p]
+    L.orc_gemm_limited.restype = ctypes.c_int
+    L.orc_gemm_limited.argtypes = [_i64, _i64, _i64, _u8p, _i64, _f32p, _i64,
+                                   _u8p, _i64, _f32p, ctypes.c_int, _i64, _i64,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   _f64p, _i64]
     L.orc_num_threads.restype = ctypes.c_int
     return L
 
@@ -210,6 +221,23 @@ class Oracle:
                "gemm")
         return d
 
+    def gemm_limited(self, a, sa, b, sb, bscale_kind, sb_s0, sb_s1, bits, chunk, interval):
+        """The GEMM on a model accumulator with `bits` significant bits
+        (chunks of `chunk` products added exactly, then the running sum cut
+        toward zero): never promoted (interval 0) or promoted to fp64 every
+        `interval` elements.  See oracle.h."""
+        a = _c(a, np.uint8)
+        b = _c(b, np.uint8)
+        sa = _c(sa, np.float32)
+        sb = _c(sb, np.float32)
+        M, K = a.shape
+        N = b.shape[0]
+        d = np.empty((M, N), np.float64)
+        _check(self.L.orc_gemm_limited(M, N, K, _p(a, _u8p), K, _p(sa, _f32p), sa.shape[1], _p(b, _u8p), K,
+                                       _p(sb, _f32p), bscale_kind, sb_s0, sb_s1, int(bits), int(chunk),
+                                       int(interval), _p(d, _f64p), N), "gemm_limited")
+        return d
+
     def gemm_entries(self, a, sa, b, sb, bscale_kind, sb_s0, sb_s1, mi, ni):
         """R[mi[i], ni[i]] for each i, as gemm() would give them."""
         a = _c(a, np.uint8)
@@ -229,6 +257,21 @@ class Oracle:
                "gemm_entries")
         return out
 
+    def gemm_abs(self, a, sa, b, sb, bscale_kind, sb_s0, sb_s1):
+        """R_abs: the same GEMM over the absolute values of the codes (sign
+        bits cleared; the scales are positive), the size of the products
+        the error bound of FP8-matrix-core partials is taken against."""
+        _check_positive(sa, "sa")
+        _check_positive(sb, "sb")
+        return self.gemm(_c(a, np.uint8) & np.uint8(0x7F), sa, _c(b, np.uint8) & np.uint8(0x7F), sb,
+                         bscale_kind, sb_s0, sb_s1)
+
+    def gemm_abs_entries(self, a, sa, b, sb, bscale_kind, sb_s0, sb_s1, mi, ni):
+        _check_positive(sa, "sa")
+        _check_positive(sb, "sb")
+        return self.gemm_entries(_c(a, np.uint8) & np.uint8(0x7F), sa, _c(b, np.uint8) & np.uint8(0x7F), sb,
+                                 bscale_kind, sb_s0, sb_s1, mi, ni)
+
     def grouped_gemm(self, offsets, a, sa, b, sb):
         """Grouped GEMM over experts: a[rows, K] codes, sa[K/128, ld] scales,
         b[G, N, K] codes, sb[G, N/128, K/128] block scales."""
@@ -246,6 +289,12 @@ class Oracle:
                                        _p(sb, _f32p), _p(d, _f64p), N),
                "grouped_gemm")
         return d
+
+    def grouped_gemm_abs(self, offsets, a, sa, b, sb):
+        """grouped_gemm over the absolute values of the codes."""
+        _check_positive(sa, "sa")
+        _check_positive(sb, "sb")
+        return self.grouped_gemm(offsets, _c(a, np.uint8) & np.uint8(0x7F), sa, _c(b, np.uint8) & np.uint8(0x7F), sb)
 
     def grouped_gemm_entries(self, offsets, a, sa, b, sb, mi, ni):
         offsets = _c(offsets, np.int32)
@@ -326,6 +375,18 @@ def grouped_gemm(offsets, a, sa, b, sb):
     return default().grouped_gemm(offsets, a, sa, b, sb)
 
 
+def gemm_limited(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, bits, chunk, interval):
+    return default().gemm_limited(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, bits, chunk, interval)
+
+
+def gemm_abs(a, sa, b, sb, bscale_kind, sb_s0, sb_s1):
+    return default().gemm_abs(a, sa, b, sb, bscale_kind, sb_s0, sb_s1)
+
+
+def grouped_gemm_abs(offsets, a, sa, b, sb):
+    return default().grouped_gemm_abs(offsets, a, sa, b, sb)
+
+
 def grouped_gemm_entries(offsets, a, sa, b, sb, mi, ni):
     return default().grouped_gemm_entries(offsets, a, sa, b, sb, mi, ni)
 
@@ -334,32 +395,7 @@ def num_threads():
     return default().num_threads()
 
 
-# ---- error metric -------------------------------------------------------------
+# ---- comparator -----------------------------------------------------------------
 
-def max_rel_err(y, r, floor_frac=1e-2):
-    """Elementwise: max |y - r| / max(|r|, floor_frac * max|r|) over all
-    elements (a plain elementwise ratio is ill-posed where r is near zero, so
-    the denominator is floored at 1% of the largest |r|).  Stricter than the
-    gate metric `normwise_err`; reported for every GEMM mode and held to the
-    gate for the exact one.  Returns 0 for an all-zero r equal to y."""
-    y = np.asarray(y, np.float64)
-    r = np.asarray(r, np.float64)
-    if r.size == 0:
-        return 0.0
-    top = float(np.max(np.abs(r)))
-    den = np.maximum(np.abs(r), floor_frac * top)
-    diff = np.abs(y - r)
-    if top == 0.0:
-        return float(np.max(diff)) if diff.size else 0.0
-    return float(np.max(diff / den))
-
-
-def normwise_err(y, r):
-    """The gate metric, max |y - r| / max |r|: the largest error relative to
-    the output's magnitude.  The pages quote a finite "maximum relative
-    error" (nearly 2%) for a K = 4096 GEMM with limited accumulation, which
-    only an error measured against the output's overall magnitude gives."""
-    y = np.asarray(y, np.float64)
-    r = np.asarray(r, np.float64)
-    top = float(np.max(np.abs(r))) if r.size else 0.0
-    return float(np.max(np.abs(y - r)) / top) if top > 0 else 0.0
+from .compare import (TOL, bound_ratio, describe, fp8_partials_bound, gate,  # noqa: E402,F401
+                      max_rel_err, measure, normwise_err, passes)

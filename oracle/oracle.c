@@ -502,6 +502,104 @@ int orc_grouped_gemm_entries(int G, int64_t N, int64_t K,
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Limited-precision accumulation: a model for the large-K study, not part of
+ * the reference result above.  The pages report that the FP8 GEMM of their
+ * tensor cores keeps only about 14 bits while it accumulates
+ * ([cameseeing-1171527], passage on the accumulation precision of FP8
+ * GEMM), that this reached a relative error of nearly 2% at K = 4096
+ * ([qna-131281], passage on the preliminary test), and that copying the
+ * partial sums to FP32 registers every 128 elements removes the problem
+ * ([why-be-59061], passage on the 128-element interval).  They give no
+ * model of that accumulator.  Reading taken: the running sum is held with
+ * `bits` significant bits; `chunk` consecutive products are added exactly
+ * (one instruction's worth), then the running sum is cut toward zero to
+ * `bits` significant bits (the bits a fixed-width aligned adder shifts out
+ * are dropped).
+ *   interval 0: never promoted -- one limited sum over all of K of the
+ *     dequantised products (dec(a) * sa) * (dec(b) * SB), each in fp64;
+ *   interval I (dividing 128): promoted every I elements -- each interval's
+ *     partial of code products dec(a) * dec(b) is formed in the limited sum
+ *     from zero, then multiplied by sa * SB of its group and added to an fp64
+ *     accumulator (fp64 standing in for the FP32 registers, whose rounding
+ *     is far below the limited sum's).
+ * ------------------------------------------------------------------------ */
+
+/* v cut toward zero to `bits` significant bits (bits >= 53: unchanged). */
+static double chop_bits(double v, int bits)
+{
+    if (v == 0.0 || bits >= 53)
+        return v;
+    int e;
+    double fr = frexp(fabs(v), &e);   /* |v| = fr * 2^e, fr in [0.5, 1) */
+    double t = floor(ldexp(fr, bits)); /* the top `bits` bits as an integer */
+    double r = ldexp(t, e - bits);
+    return v < 0 ? -r : r;
+}
+
+/* Add products p[0..n-1] to acc in chunks of `chunk`: each chunk is summed
+ * exactly (fp64; the products here are exact and a chunk's sum of at most 128
+ * of them is too), then the running sum is cut to `bits` bits. */
+static double limited_sum(double acc, const double *p, int64_t n, int chunk,
+                          int bits)
+{
+    for (int64_t i = 0; i < n; i += chunk) {
+        double c = 0.0;
+        for (int64_t j = i; j < i + chunk && j < n; j++)
+            c += p[j];
+        acc = chop_bits(acc + c, bits);
+    }
+    return acc;
+}
+
+int orc_gemm_limited(int64_t M, int64_t N, int64_t K, const uint8_t *a,
+                     int64_t lda, const float *sa, int64_t ldsa,
+                     const uint8_t *b, int64_t ldb, const float *sb,
+                     int bscale_kind, int64_t sb_s0, int64_t sb_s1, int bits,
+                     int chunk, int interval, double *d, int64_t ldd)
+{
+    if (!a || !sa || !b || !sb || !d || M < 0 || N < 0 || K < 0 ||
+        (bscale_kind != 0 && bscale_kind != 1) || bits < 2 || chunk < 1 ||
+        interval < 0)
+        return ORC_ERR_ARG;
+    if (K % 128 != 0 || (interval > 0 && (128 % interval != 0 || interval % chunk != 0)))
+        return ORC_ERR_SHAPE;
+    double dec[256]; /* decoded values, so the loops below stay cheap */
+    for (int c = 0; c < 256; c++)
+        dec[c] = orc_e4m3_decode((uint8_t)c);
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; m++) {
+        double *prod = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        const uint8_t *arow = a + m * lda;
+        for (int64_t n = 0; n < N; n++) {
+            const uint8_t *brow = b + n * ldb;
+            double out;
+            if (interval == 0) {
+                for (int64_t k = 0; k < K; k++) {
+                    int64_t g = k / 128;
+                    double x = dec[arow[k]] * (double)sa[g * ldsa + m];
+                    double y = dec[brow[k]] * sb_at(sb, bscale_kind, sb_s0, sb_s1, n, g);
+                    prod[k] = x * y;
+                }
+                out = limited_sum(0.0, prod, K, chunk, bits);
+            } else {
+                out = 0.0;
+                for (int64_t k0 = 0; k0 < K; k0 += interval) {
+                    int64_t g = k0 / 128;
+                    for (int64_t k = k0; k < k0 + interval; k++)
+                        prod[k - k0] = dec[arow[k]] * dec[brow[k]];
+                    double part = limited_sum(0.0, prod, interval, chunk, bits);
+                    out += part * ((double)sa[g * ldsa + m] * sb_at(sb, bscale_kind, sb_s0, sb_s1, n, g));
+                }
+            }
+            d[m * ldd + n] = out;
+        }
+        free(prod);
+    }
+    return ORC_OK;
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -136,6 +136,20 @@ int orc_grouped_gemm_entries(int G, int64_t N, int64_t K,
                              const int64_t *mi, const int64_t *ni,
                              double *out);
 
+/* A model of FP8 GEMM accumulation with limited precision, for the large-K
+ * study (not the reference result): the running sum keeps `bits`
+ * significant bits, `chunk` products are added exactly and the sum is then
+ * cut toward zero to `bits` bits.  interval 0: one such sum over all of K
+ * of the dequantised products (never promoted); interval I (dividing 128,
+ * a multiple of chunk): each I-element partial of code products is such a
+ * sum from zero, then scaled by its group's sa * SB and added in fp64
+ * (promoted every I elements).  Arguments otherwise as orc_gemm. */
+int orc_gemm_limited(int64_t M, int64_t N, int64_t K, const uint8_t *a,
+                     int64_t lda, const float *sa, int64_t ldsa,
+                     const uint8_t *b, int64_t ldb, const float *sb,
+                     int bscale_kind, int64_t sb_s0, int64_t sb_s1, int bits,
+                     int chunk, int interval, double *d, int64_t ldd);
+
 /* Number of OpenMP threads the GEMM and quantiser loops use (1 when the
  * library was built without OpenMP). */
 int orc_num_threads(void);

@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: host <-> device moves, cached workload
-inputs and the edge-case inputs.  No method arithmetic here."""
+inputs, the edge-case inputs and the one gate every GEMM test applies
+(the comparator itself lives in oracle/compare.py).  No method arithmetic
+here."""
 import functools
 import sys
 
@@ -10,6 +12,15 @@ import torch
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def check(y, r, rabs, out, accum, groups, tag):
+    """Gate a GPU GEMM output y (float64 values) against the oracle's r with
+    the comparator of oracle/compare.py, logging every measure."""
+    import oracle
+    ok, why, m = oracle.gate(y, r, rabs, out, accum, groups)
+    log(f"{tag}: {oracle.describe(m, out)}")
+    assert ok, (tag, why, m)
 
 
 def dev_bf16(bits):

@@ -579,6 +579,66 @@ def check_scale_edges(orc):
     assert orc.group_scale(224.5, 1)[0] == np.float32(1.0)
 
 
+# ---- limited-precision accumulation model -------------------------------------------
+
+def load_limited():
+    rows = []
+    with open(os.path.join(GOLDEN, "limited_accumulation.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            name, K, first, rest, bits, chunk, interval, want = line.split()
+            rows.append((name, int(K), int(first, 16), int(rest, 16), int(bits), int(chunk), int(interval),
+                         float(want)))
+    return rows
+
+
+def check_limited_worked(orc):
+    """The model of limited accumulation on the hand-worked cases of
+    tests/golden/limited_accumulation.txt (swamping of small products by a
+    large one, cutting toward zero, exact chunks, promotion intervals)."""
+    rows = load_limited()
+    assert len(rows) >= 9
+    for name, K, first, rest, bits, chunk, interval, want in rows:
+        a = np.full((1, K), rest, np.uint8)
+        a[0, 0] = first
+        b = np.full((1, K), 0x38, np.uint8)
+        sa = np.ones((K // 128, 1), np.float32)
+        sb = np.ones((1, K // 128), np.float32)
+        got = orc.gemm_limited(a, sa, b, sb, 0, K // 128, 1, bits, chunk, interval)
+        assert got[0, 0] == want, (name, got[0, 0], want)
+
+
+def check_limited_reduces_to_exact(orc, seed=67):
+    """With 53 bits the model is the plain sum: promoted every 128 elements
+    it equals the oracle's GEMM bit for bit (each group partial is exact in
+    fp64 and is scaled and added in the same order), and never promoted with
+    unit scales it equals the exact integer-unit sum too; fewer bits never
+    beat the exact result on these inputs by construction of the cut
+    (|limited| <= |exact| for a sum of same-sign products)."""
+    rng = np.random.default_rng(seed)
+    table = orc.decode_table()
+    M, N, K = 5, 140, 512
+    a = _random_codes(rng, (M, K), table)
+    b = _random_codes(rng, (N, K), table)
+    sa = rng.uniform(0.1, 4, (K // 128, M)).astype(np.float32)
+    sbk = rng.uniform(0.1, 4, ((N + 127) // 128, K // 128)).astype(np.float32)
+    exact = orc.gemm(a, sa, b, sbk, 0, sbk.shape[1], 1)
+    np.testing.assert_array_equal(orc.gemm_limited(a, sa, b, sbk, 0, sbk.shape[1], 1, 53, 1, 128), exact)
+    sbc = rng.uniform(0.1, 4, (K // 128, N)).astype(np.float32)
+    np.testing.assert_array_equal(orc.gemm_limited(a, sa, b, sbc, 1, N, 0, 53, 4, 128),
+                                  orc.gemm(a, sa, b, sbc, 1, N, 0))
+    ones_a = np.ones((K // 128, M), np.float32)
+    ones_b = np.ones((2, K // 128), np.float32)
+    np.testing.assert_array_equal(orc.gemm_limited(a, ones_a, b, ones_b, 0, K // 128, 1, 53, 1, 0),
+                                  orc.gemm(a, ones_a, b, ones_b, 0, K // 128, 1))
+    pos_a, pos_b = a & np.uint8(0x7F), b & np.uint8(0x7F)
+    lim = orc.gemm_limited(pos_a, sa, pos_b, sbk, 0, sbk.shape[1], 1, 10, 1, 0)
+    full = orc.gemm(pos_a, sa, pos_b, sbk, 0, sbk.shape[1], 1)
+    assert np.all(lim <= full) and np.all(lim >= full * (1 - 2.0 ** -9 * K))
+
+
 ALL_CHECKS = [
     check_decode_table, check_round_trip, check_anchors, check_worked_examples,
     check_quant_bruteforce, check_amax_maps_to_448, check_pow2_exact,
@@ -587,4 +647,5 @@ ALL_CHECKS = [
     check_gemm_integers, check_gemm_entries_and_grouped, check_scale_edges,
     check_requant_bruteforce, check_requant_exact_dequant, check_requant_fp32_dequant,
     check_grouped_col_aligned, check_grouped_col_partial,
+    check_limited_worked, check_limited_reduces_to_exact,
 ]

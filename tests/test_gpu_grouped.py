@@ -5,30 +5,11 @@ import torch
 
 import oracle
 from block_scaled_gemm_amd import inputs
-from gpu_util import workload, bf16_f64, dev, dev_bf16, host, log
+from gpu_util import workload, bf16_f64, check, dev, dev_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 ACCUMS = pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
 ACCUMS_POW2 = pytest.mark.parametrize("accum", [0, 1, 2], ids=["acc32", "mfma8", "mfma8pow2"])
-
-
-def check(y, r, rabs, out, accum, groups, tag):
-    """Gate, every mode: max|D - R| / max|R| <= 1e-3 (fp32 out) or 8e-3
-    (bf16 out).  The exact mode is also held to the elementwise error with
-    a 1%-of-max floor; the FP8-matrix-core modes to their error bound."""
-    err = oracle.normwise_err(y, r)
-    elem = oracle.max_rel_err(y, r)
-    tol = 1e-3 if out == 1 else 8e-3
-    if accum == 0:
-        log(f"{tag}: max rel err {err:.3e}, elementwise {elem:.3e} (gate {tol:.0e})")
-        assert elem <= tol, (tag, elem)
-    else:
-        rnd = 2.0 ** -8 * np.abs(r) if out == 0 else 2.0 ** -23 * np.abs(r)
-        bound = 2.0 ** -10 * rabs + groups * 2.0 ** -23 * rabs + rnd + 1e-30
-        ratio = float(np.max(np.abs(y - r) / bound))
-        log(f"{tag}: max rel err {err:.3e}, elementwise {elem:.3e} (gate {tol:.0e}); error / bound {ratio:.3f}")
-        assert ratio <= 1.0, (tag, ratio)
-    assert err <= tol, (tag, err)
 
 
 def out_f64(t):
@@ -63,7 +44,7 @@ def test_grouped_small_with_empty_experts(hip, orc, out, accum):
     qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
     y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, out, accum=accum)
     r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
-    rabs = orc.grouped_gemm(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw)
+    rabs = orc.grouped_gemm_abs(offsets, wqx, wsx, wqw, wsw)
     for e in range(len(counts)):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
@@ -84,7 +65,7 @@ def test_grouped_short_k(hip, orc, K, accum):
     qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
     y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 1, accum=accum)
     r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
-    rabs = orc.grouped_gemm(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw)
+    rabs = orc.grouped_gemm_abs(offsets, wqx, wsx, wqw, wsw)
     check(out_f64(y), r, rabs, 1, accum, K // 128, f"short K={K} accum={accum}")
 
 
@@ -108,7 +89,7 @@ def _check_full(hip, orc, data, mode, tag, accum):
     qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, mode)
     y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, 0, accum=accum)
     r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
-    rabs = orc.grouped_gemm(offsets, wqx & 0x7F, wsx, wqw & 0x7F, wsw)
+    rabs = orc.grouped_gemm_abs(offsets, wqx, wsx, wqw, wsw)
     check(out_f64(y), r, rabs, 0, accum, wqw.shape[2] // 128, f"{tag} accum={accum}")
 
 
@@ -149,13 +130,13 @@ def _moe_dgrad_case(hip, orc, dY, W, offsets, accum, tag, sample=None):
         sbe = np.ascontiguousarray(wsw[e * Nw // 128:(e + 1) * Nw // 128])
         if sample is None:
             r = orc.gemm(a, sa, b, sbe, 0, 1, sbe.shape[1])
-            rabs = orc.gemm(a & 0x7F, sa, b & 0x7F, sbe, 0, 1, sbe.shape[1])
+            rabs = orc.gemm_abs(a, sa, b, sbe, 0, 1, sbe.shape[1])
             got = y[r0:r1]
         else:
             rng = np.random.default_rng(e)
             mi, ni = rng.integers(0, r1 - r0, sample), rng.integers(0, Kw, sample)
             r = orc.gemm_entries(a, sa, b, sbe, 0, 1, sbe.shape[1], mi, ni)
-            rabs = orc.gemm_entries(a & 0x7F, sa, b & 0x7F, sbe, 0, 1, sbe.shape[1], mi, ni)
+            rabs = orc.gemm_abs_entries(a, sa, b, sbe, 0, 1, sbe.shape[1], mi, ni)
             got = y[r0:r1][mi, ni]
         check(got, r, rabs, 1, accum, Nw // 128, f"{tag} expert {e}")
 
@@ -205,6 +186,23 @@ def test_quant_grouped_col_small(hip, orc, mode):
     np.testing.assert_array_equal(host(s)[:tp // 128], ws)
 
 
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
+def test_quant_grouped_col_upproj_full_size(hip, orc, mode):
+    """128x1 groups per expert at the up-projection's real size: dY[rows x
+    4096] and X[rows x 7168] of the 32 experts (as the MoE Wgrad quantises
+    them), every code, padding byte and scale bit-exact."""
+    data = workload("grouped_upproj")
+    offsets = data["offsets"]
+    dY = inputs.random_bf16(224, (int(offsets[-1]), 4096), sd=1e-3)
+    for name, x in (("dY", dY), ("X", data["Xcat"])):
+        q, s = hip.fp8_quant_tile_grouped_col(dev_bf16(x), dev(offsets), mode)
+        wq, ws = orc.quant_tile_grouped_col(x, offsets, mode)
+        tp = wq.shape[1]
+        np.testing.assert_array_equal(host(q)[:, :tp], wq)
+        np.testing.assert_array_equal(host(s)[:tp // 128].view(np.uint32), ws.view(np.uint32))
+        log(f"grouped 128x1 {name}[{x.shape[0]}x{x.shape[1]}] mode={mode}: {wq.size} codes bit-exact")
+
+
 def _moe_wgrad_check(hip, orc, dY, X, offsets, accum, tag, sample=None, mode=0):
     counts = np.diff(offsets)
     dw = hip.moe_wgrad(dev(offsets), dev_bf16(dY), dev_bf16(X), mode, out_dtype=1, accum=accum)
@@ -221,13 +219,13 @@ def _moe_wgrad_check(hip, orc, dY, X, offsets, accum, tag, sample=None, mode=0):
         b, sb = np.ascontiguousarray(wqx[:, k0:k1]), np.ascontiguousarray(wsx[k0 // 128:k1 // 128])
         if sample is None:
             r = orc.gemm(a, sa, b, sb, 1, sb.shape[1], 0)
-            rabs = orc.gemm(a & 0x7F, sa, b & 0x7F, sb, 1, sb.shape[1], 0)
+            rabs = orc.gemm_abs(a, sa, b, sb, 1, sb.shape[1], 0)
             got = host(dw[e]).astype(np.float64)
         else:
             rng = np.random.default_rng(e)
             mi, ni = rng.integers(0, N, sample), rng.integers(0, C, sample)
             r = orc.gemm_entries(a, sa, b, sb, 1, sb.shape[1], 0, mi, ni)
-            rabs = orc.gemm_entries(a & 0x7F, sa, b & 0x7F, sb, 1, sb.shape[1], 0, mi, ni)
+            rabs = orc.gemm_abs_entries(a, sa, b, sb, 1, sb.shape[1], 0, mi, ni)
             got = dw[e][torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy().astype(np.float64)
         check(got, r, rabs, 1, accum, (k1 - k0) // 128, f"{tag} expert {e}")
 

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from block_scaled_gemm_amd import inputs
-from gpu_util import workload, dev, dev_bf16, edge_rows, host, log
+from gpu_util import check, workload, dev, dev_bf16, edge_rows, host, log
 
 pytestmark = pytest.mark.gpu
 MODES = pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
@@ -76,10 +76,11 @@ def test_requant_into_strided_outputs(hip, orc):
     assert torch.all(qt[:, 256:] == 0xAB).item() and torch.all(st[:, 256:] == -1.0).item()
 
 
-def test_requant_full_size_and_wgrad(hip, orc):
+@pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
+def test_requant_full_size_and_wgrad(hip, orc, accum):
     """Expert-backward X[8192 x 7168]: 1x128 codes from the forward pass
     re-tiled to 128x1 (all codes and scales compared), then Wgrad dW = dY^T X
-    on the re-tiled operand, fp32 out, sampled against the oracle."""
+    on the re-tiled operand, fp32 out, every output against the oracle."""
     d = workload("expert_backward")
     q, s = hip.fp8_quant_tile(dev_bf16(d["X"]), hip.AXIS_ROW, 0)
     wq, ws = orc.quant_tile(d["X"], 0, 0)
@@ -91,14 +92,10 @@ def test_requant_full_size_and_wgrad(hip, orc):
     qdt, sdt = hip.fp8_quant_tile(dev_bf16(d["dY"]), hip.AXIS_COL, 0)
     wqdt, wsdt = orc.quant_tile(d["dY"], 1, 0)
     np.testing.assert_array_equal(host(qdt), wqdt)
-    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, 1)
-    rng = np.random.default_rng(6)
-    mi, ni = rng.integers(0, 2048, 3000), rng.integers(0, 7168, 3000)
-    r = orc.gemm_entries(wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0, mi, ni)
-    y = host(dw)[mi, ni].astype(np.float64)
-    err = oracle.max_rel_err(y, r)
-    log(f"wgrad on re-tiled X: max rel err {err:.3e}")
-    assert err <= 1e-3
+    dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, 1, accum=accum)
+    r = orc.gemm(wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
+    rabs = orc.gemm_abs(wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
+    check(host(dw).astype(np.float64), r, rabs, 1, accum, 64, f"wgrad on re-tiled X accum={accum}")
 
 
 @MODES

@@ -81,6 +81,15 @@ MUTATIONS = {
     "grouped_col_unpadded_start": (
         "        start += ng * 128;",
         "        start += n;"),
+    "limited_cut_to_nearest": (
+        "double t = floor(ldexp(fr, bits)); /* the top `bits` bits as an integer */",
+        "double t = floor(ldexp(fr, bits) + 0.5);"),
+    "limited_partial_not_restarted": (
+        "double part = limited_sum(0.0, prod, interval, chunk, bits);",
+        "double part = limited_sum(out, prod, interval, chunk, bits) - out;"),
+    "limited_chunk_ignored": (
+        "        for (int64_t j = i; j < i + chunk && j < n; j++)",
+        "        for (int64_t j = i; j < i + 1 && j < n; j++)"),
     "b_reversed_within_group": (
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[k]];",
         "p += (int64_t)dec_units[arow[k]] * (int64_t)dec_units[brow[g * 128 + 127 - (k - g * 128)]];"),
