@@ -187,20 +187,24 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
 
 }  // namespace
 
-FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
-                                      const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
-                                      const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1, void* d,
-                                      int64_t ldd, int out_dtype, int accum, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks of the dense GEMM apart from the workspace.
+int check_gemm_dense(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                     const uint8_t* b, int64_t ldb, const float* sb, int bscale_kind, void* d, int64_t ldd,
+                     int out_dtype, int accum) {
     if (bscale_kind != FP8BS_BSCALE_BLOCK && bscale_kind != FP8BS_BSCALE_TILE) return FP8BS_ERR_ARG;
     if (accum != FP8BS_ACCUM_FP32 && accum != FP8BS_ACCUM_MFMA8 && accum != FP8BS_ACCUM_MFMA8_POW2)
         return FP8BS_ERR_ARG;
-    if (int r = check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype)) return r;
-    if (M == 0 || N == 0) return FP8BS_OK;
-    const size_t need = fp8_gemm_workspace_bytes(M, N, K);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return FP8BS_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
-    if (int r = check_device()) return r;
+    return check_gemm_common(M, N, K, a, lda, sa, ldsa, b, ldb, sb, d, ldd, out_dtype);
+}
+
+// Enqueue a validated dense GEMM; `ws` holds fp8_gemm_workspace_bytes(M, N, K)
+// bytes (unused when that is 0).
+int launch_dense_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                      int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb, int bscale_kind, int64_t sb_s0,
+                      int64_t sb_s1, void* d, int64_t ldd, int out_dtype, int accum, void* ws, size_t need,
+                      void* stream) {
     fp8bs::GemmArgs g{};
     g.M = M;
     g.N = N;
@@ -220,9 +224,27 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
     g.out_f32 = out_dtype == FP8BS_OUT_F32;
     g.accum = accum;
     g.splits = need > 0 ? fp8bs::gemm_splits(M, N, K) : 1;
-    g.ws = (float*)workspace;
+    g.ws = (float*)ws;
     g.ws_ld = (N + 3) / 4 * 4;
     return hip_status(fp8bs::launch_gemm(g, (hipStream_t)stream));
+}
+
+}  // namespace
+
+FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                      const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                      const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1, void* d,
+                                      int64_t ldd, int out_dtype, int accum, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (int r = check_gemm_dense(M, N, K, a, lda, sa, ldsa, b, ldb, sb, bscale_kind, d, ldd, out_dtype, accum))
+        return r;
+    if (M == 0 || N == 0) return FP8BS_OK;
+    const size_t need = fp8_gemm_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP8BS_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+    if (int r = check_device()) return r;
+    return launch_dense_gemm(M, N, K, a, lda, sa, ldsa, b, ldb, sb, bscale_kind, sb_s0, sb_s1, d, ldd, out_dtype,
+                             accum, workspace, need, stream);
 }
 
 FP8BS_EXPORT int fp8_gemm_blockscaled_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
@@ -237,6 +259,7 @@ FP8BS_EXPORT int fp8_gemm_blockscaled_quant(int64_t M, int64_t N, int64_t K, con
     if (M < 0 || N < 0 || K < 0) return FP8BS_ERR_ARG;
     if (M > 0 && N > 0 && (!q || !s || (K > 0 && (!a || !sa || !b || !sb)))) return FP8BS_ERR_ARG;
     if (K % 128 != 0 || N % 128 != 0) return FP8BS_ERR_SHAPE;
+    if (lda > FP8BS_MAX_LD || ldb > FP8BS_MAX_LD) return FP8BS_ERR_SHAPE;  // 32-bit per-lane row offsets
     if (lda < K || ldb < K || ldq < N || ldsa < M || lds < M) return FP8BS_ERR_ARG;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(q, 4) || !aligned(sa, 4) || !aligned(sb, 4) ||
         !aligned(s, 4) || (K > 0 && (lda % 16 != 0 || ldb % 16 != 0)) || ldq % 4 != 0)

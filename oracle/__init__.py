@@ -90,6 +90,8 @@ def _declare(L):
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    _f64p, _i64]
     L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [ctypes.c_int]
     return L
 
 
@@ -317,6 +319,10 @@ class Oracle:
 
     def num_threads(self):
         return int(self.L.orc_num_threads())
+
+    def set_num_threads(self, n):
+        """Threads for later calls (n < 1: back to the default)."""
+        self.L.orc_set_num_threads(int(n))
 
 
 _default = None

@@ -600,6 +600,19 @@ int orc_gemm_limited(int64_t M, int64_t N, int64_t K, const uint8_t *a,
     return ORC_OK;
 }
 
+/* Threads for the OpenMP loops of later calls (n < 1 restores the default). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0)
+        dflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -154,6 +154,9 @@ int orc_gemm_limited(int64_t M, int64_t N, int64_t K, const uint8_t *a,
  * library was built without OpenMP). */
 int orc_num_threads(void);
 
+/* Threads the OpenMP loops of later calls use (n < 1: the default). */
+void orc_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

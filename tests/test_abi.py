@@ -163,6 +163,9 @@ def _gq(**kw):
     (dict(kind=2), ARG), (dict(mode=2), ARG), (dict(acc=3), ARG), (dict(q=None), ARG), (dict(s=None), ARG),
     (dict(ldq=128), ARG), (dict(lds=100), ARG), (dict(N=200, ldq=256), SHAPE), (dict(K=500, lda=512, ldb=512), SHAPE),
     (dict(q=FAKE + 2), ALIGN), (dict(ldq=258), ALIGN), (dict(s=FAKE + 1), ALIGN), (dict(M=0), OK),
+    # code strides above the 32-bit per-lane row offsets, as for the plain GEMM
+    (dict(lda=(1 << 24) + 16), SHAPE), (dict(ldb=(1 << 24) + 16), SHAPE), (dict(M=0, lda=(1 << 24) + 16), SHAPE),
+    (dict(M=0, lda=1 << 24, ldb=1 << 24), OK),
 ])
 def test_gemm_quant_validation(kw, want):
     assert _gq(**kw) == want

@@ -55,3 +55,45 @@ def test_traffic_is_used_only_for_the_source_it_was_measured_on(tmp_path, monkey
     assert bench.measured_traffic(kernel) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
     assert bench.measured_traffic(kernel) is None
+
+
+def _tiny_sample():
+    import numpy as np
+    import oracle
+    from block_scaled_gemm_amd import inputs
+    orc = oracle.default()
+    d = inputs.tiny_fprop()
+    qx, sx = orc.quant_tile(d["X"], 0, 0)
+    qw, sw, _ = orc.quant_block(d["W"], 0)
+    r = orc.gemm(qx, sx, qw, sw, 0, sw.shape[1], 1)
+    y = inputs.bf16_bits(r.astype(np.float32))
+    return {"ms": 128, "ns": 256, "qx": qx, "sx": sx, "qw": qw, "sw": sw, "r": r}, y
+
+
+def test_parity_reports_the_comparator_and_the_codes(monkeypatch):
+    """bench.parity on the tiny Fprop: the oracle's own result rounded to
+    bf16 passes in every mode; a changed code or a changed output fails."""
+    import numpy as np
+    monkeypatch.setattr(bench, "K", 512)
+    sample, y = _tiny_sample()
+    for accum in (0, 1):
+        p = bench.parity(sample, y, sample["qx"], sample["sx"], sample["qw"], sample["sw"], accum)
+        assert p["gate_passed"] and p["codes_scales_bitexact"], p
+        assert p["normwise"] <= 2.0 ** -8 and p["elementwise_within_tol"]
+    qx = sample["qx"].copy()
+    qx[5, 7] ^= 0x80
+    p = bench.parity(sample, y, qx, sample["sx"], sample["qw"], sample["sw"], 1)
+    assert not p["codes_scales_bitexact"] and not p["gate_passed"]
+    y2 = y.copy()
+    y2[3, 4] ^= 0x8000  # flip the sign of one bf16 output
+    p = bench.parity(sample, y2, sample["qx"], sample["sx"], sample["qw"], sample["sw"], 1)
+    assert p["codes_scales_bitexact"] and not p["gate_passed"]
+
+
+def test_cpu_quant_baseline_reports_both_thread_counts():
+    from block_scaled_gemm_amd import inputs
+    d = inputs.tiny_fprop()
+    q = bench.cpu_quant_baseline(d["X"], d["W"], reps=1)
+    for name in ("quant_tile_row_X", "quant_block_W"):
+        assert q[name]["GB/s_1_thread"] > 0 and q[name]["GB/s_all_threads"] > 0
+        assert q[name]["threads"] >= 1
