@@ -13,6 +13,7 @@ Functions carry the C names (see include/fp8bs.h for the full contract):
     fp8_quant_dual(x, scale_mode)                   -> (qr, sr, qc, sc)
     fp8_requant_col(q, s, scale_mode)               -> (qt, st)
     fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype) -> d
+    fp8_gemm_blockscaled_noalloc(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, d)  -> d
     fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype, rows_bound=None)    -> d
     fp8_grouped_gemm_strided(offsets, a, sa, G, N, b, ldb, b_estride, sb, ...) -> d
 
@@ -32,6 +33,7 @@ SCALE_FP32, SCALE_POW2 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 BSCALE_BLOCK, BSCALE_TILE = 0, 1
 ACCUM_FP32, ACCUM_MFMA8, ACCUM_MFMA8_POW2 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FP8BS_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -71,6 +73,9 @@ def lib():
         L.fp8_gemm_blockscaled.restype = i32
         L.fp8_gemm_blockscaled.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32,
                                            i64, i64, vp, i64, i32, i32, vp, ctypes.c_size_t, vp]
+        L.fp8_gemm_blockscaled_noalloc.restype = i32
+        L.fp8_gemm_blockscaled_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32,
+                                                   i64, i64, vp, i64, i32, i32, vp]
         L.fp8_grouped_gemm.restype = i32
         L.fp8_grouped_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp, vp,
                                        i64, i32, i32, vp]
@@ -256,6 +261,28 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_
                                       _ld(d), int(out_dtype), int(accum),
                                       _ptr(workspace) if workspace is not None else None, ws_bytes,
                                       _stream()), "fp8_gemm_blockscaled")
+    return d
+
+
+def fp8_gemm_blockscaled_noalloc(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, d, out_dtype=OUT_BF16,
+                                 accum=ACCUM_FP32):
+    """fp8_gemm_blockscaled into a caller-allocated d, with no workspace: the
+    library's own per-GPU scratch array holds the split-K partials (shapes
+    needing more than NOALLOC_SCRATCH_BYTES are rejected).  Calls that
+    overlap on one GPU share that array."""
+    _dev(a, "a", torch.uint8)
+    _dev(b, "b", torch.uint8)
+    _dev(sa, "sa", torch.float32)
+    _dev(sb, "sb", torch.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    _dev(d, "d", torch.float32 if out_dtype == OUT_F32 else torch.bfloat16)
+    _check(lib().fp8_gemm_blockscaled_noalloc(M, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa), _ptr(b), _ld(b),
+                                              _ptr(sb), int(bscale_kind), int(sb_s0), int(sb_s1), _ptr(d), _ld(d),
+                                              int(out_dtype), int(accum), _stream()),
+           "fp8_gemm_blockscaled_noalloc")
     return d
 
 

@@ -247,6 +247,56 @@ FP8BS_EXPORT int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uin
                              accum, workspace, need, stream);
 }
 
+// ---- the dense GEMM without a caller workspace ---------------------------------------
+//
+// For callers that cannot allocate device memory: the split-K partials live
+// in this file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is only a host-side stand-in, so it is never used as
+// an address: at the first call on a device (with that device current)
+// hipGetSymbolAddress gives that device's copy, which is kept per device and
+// passed to the kernels.  Nothing here needs to start at zero (every split
+// writes its whole partial before the reduction reads it).
+static __device__ __align__(256) uint8_t scratch[FP8BS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex scratch_mu;
+void* scratch_ptr[64];
+
+int device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8BS_ERR_DEVICE;
+    if (dev >= 64) return FP8BS_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8BS_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return FP8BS_OK;
+}
+
+}  // namespace
+
+FP8BS_EXPORT int fp8_gemm_blockscaled_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                              const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                              const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1,
+                                              void* d, int64_t ldd, int out_dtype, int accum, void* stream) {
+    if (int r = check_gemm_dense(M, N, K, a, lda, sa, ldsa, b, ldb, sb, bscale_kind, d, ldd, out_dtype, accum))
+        return r;
+    if (M == 0 || N == 0) return FP8BS_OK;
+    const size_t need = fp8_gemm_workspace_bytes(M, N, K);
+    if (need > (size_t)FP8BS_NOALLOC_SCRATCH_BYTES) return FP8BS_ERR_WORKSPACE;
+    if (int r = check_device()) return r;
+    void* ws = nullptr;
+    if (need > 0)
+        if (int r = device_scratch(&ws)) return r;
+    return launch_dense_gemm(M, N, K, a, lda, sa, ldsa, b, ldb, sb, bscale_kind, sb_s0, sb_s1, d, ldd, out_dtype,
+                             accum, ws, need, stream);
+}
+
 FP8BS_EXPORT int fp8_gemm_blockscaled_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                                             const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
                                             const float* sb, int bscale_kind, int64_t sb_s0, int64_t sb_s1,

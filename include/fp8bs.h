@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 3
+#define FP8BS_ABI_VERSION 4
 
 /* Largest lda / ldb (bytes) the GEMMs take: the kernels address the rows of
  * a 256-row tile with 32-bit offsets (255 * 2^24 + 127 < 2^32). */
@@ -311,6 +311,38 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t *a,
 
 /* Workspace bytes fp8_gemm_blockscaled needs for this shape (0 = none). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Size of the device scratch array each GPU holds for
+ * fp8_gemm_blockscaled_noalloc: 16 MiB (the split-K partials of a
+ * 256 x 256 output over K = 65536). */
+#define FP8BS_NOALLOC_SCRATCH_BYTES (16LL << 20)
+
+/*
+ * fp8_gemm_blockscaled_noalloc -- fp8_gemm_blockscaled for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving
+ * loops that must not call the allocator, harnesses that forbid it.  It
+ * takes no workspace: the split-K partials that fp8_gemm_blockscaled keeps
+ * in the caller's workspace go to a device array of
+ * FP8BS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, at the
+ * first call on that device).  The call allocates and frees nothing and
+ * gives the same results as fp8_gemm_blockscaled (the same kernels and split
+ * count).  Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (different streams, or several host threads)
+ * race on it and give undefined results; calls on one stream are ordered.
+ * Arguments, layouts and alignment as fp8_gemm_blockscaled.
+ * Errors: as fp8_gemm_blockscaled; ERR_WORKSPACE when the shape needs more
+ * than FP8BS_NOALLOC_SCRATCH_BYTES (fp8_gemm_workspace_bytes(M, N, K)
+ * above it); ERR_HIP when the array's address cannot be obtained.
+ */
+int fp8_gemm_blockscaled_noalloc(int64_t M, int64_t N, int64_t K,
+                                 const uint8_t *a, int64_t lda,
+                                 const float *sa, int64_t ldsa,
+                                 const uint8_t *b, int64_t ldb,
+                                 const float *sb, int bscale_kind,
+                                 int64_t sb_s0, int64_t sb_s1, void *d,
+                                 int64_t ldd, int out_dtype, int accum,
+                                 void *stream);
 
 /*
  * fp8_gemm_blockscaled_quant -- the block-scaled GEMM with its output

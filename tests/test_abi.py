@@ -26,7 +26,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
               "fp8_grouped_gemm_strided", "fp8_quant_tile_grouped_col", "fp8_grouped_gemm_kgrouped",
-              "fp8_gemm_blockscaled_quant",
+              "fp8_gemm_blockscaled_quant", "fp8_gemm_blockscaled_noalloc",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -46,7 +46,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bs.abi_version() == 3
+    assert bs.abi_version() == 4
     for s in range(7):
         assert bs.status_string(s)
     assert "unknown" in bs.status_string(99)
@@ -148,6 +148,38 @@ def _gemm(**kw):
 ])
 def test_gemm_validation(kw, want):
     assert _gemm(**kw) == want
+
+
+def _gna(**kw):
+    a = dict(M=256, N=256, K=512, a=FAKE, lda=512, sa=FAKE, ldsa=256, b=FAKE, ldb=512, sb=FAKE,
+             kind=0, s0=4, s1=1, d=FAKE, ldd=256, out=0, acc=0)
+    a.update(kw)
+    return bs.lib().fp8_gemm_blockscaled_noalloc(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["ldsa"],
+                                                 a["b"], a["ldb"], a["sb"], a["kind"], a["s0"], a["s1"], a["d"],
+                                                 a["ldd"], a["out"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kind=2), ARG), (dict(out=2), ARG), (dict(acc=3), ARG), (dict(a=None), ARG), (dict(d=None), ARG),
+    (dict(M=-1), ARG), (dict(lda=256), ARG), (dict(ldd=128), ARG), (dict(ldsa=100), ARG),
+    (dict(K=500, lda=512, ldb=512), SHAPE), (dict(a=FAKE + 8), ALIGN), (dict(d=FAKE + 4), ALIGN),
+    (dict(lda=(1 << 24) + 16), SHAPE), (dict(M=0), OK), (dict(N=0), OK),
+    # split-K partials above the library's scratch array: 64 splits of a
+    # 512 x 256 output (32 MiB) are refused before any device call
+    (dict(M=512, N=256, K=65536, lda=65536, ldb=65536, ldsa=512), WORKSPACE),
+])
+def test_gemm_noalloc_validation(kw, want):
+    assert _gna(**kw) == want
+
+
+def test_noalloc_scratch_covers_the_large_k_workload():
+    """The scratch array holds the split-K partials of the 256 x 256 x 65536
+    GEMM, and the binding's constant matches the header's."""
+    text = open(HEADER).read()
+    assert "#define FP8BS_NOALLOC_SCRATCH_BYTES (16LL << 20)" in text
+    assert bs.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert 0 < bs.gemm_workspace_bytes(256, 256, 65536) <= bs.NOALLOC_SCRATCH_BYTES
+    assert bs.gemm_workspace_bytes(512, 256, 65536) > bs.NOALLOC_SCRATCH_BYTES
 
 
 def _gq(**kw):
