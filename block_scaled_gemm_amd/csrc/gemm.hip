@@ -483,8 +483,10 @@ struct Sub {
 // would run their MFMA blocks and their promotion FMAs in step; the second
 // one starts the group's MFMA work about 64 cycles later, so that its MFMAs
 // overlap the first one's FMAs.  On the dense Fprop with FP32 scales: 2-3%
-// faster on average over six paired runs (run-to-run spread is about 2%);
-// no gain measured in the other loops, which do not use it.
+// faster on average over six paired runs (run-to-run spread is about 2%).
+// The per-column (Wgrad) loop, which issues a fragment's MFMAs before their
+// promotion, uses it too: with it that loop ran 4-6% faster on the expert
+// Wgrad in three paired runs.
 __device__ __forceinline__ void offset_second_wave() {
     if (threadIdx.x >= THREADS / 2) __builtin_amdgcn_s_sleep(1);
 }
@@ -537,16 +539,20 @@ __device__ __forceinline__ void compute_mfma8(const uint8_t* stage, int wm, int 
                 }
             }
         } else {
+            // per-column scales: the MI MFMAs of a fragment first, then their
+            // promotion (two multiplies per output), so one wave's VALU phase
+            // can run beside the other wave's MFMA phase on the SIMD
+            offset_second_wave();
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
                 const v8i bf = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
-                v4f sbn;
-                sbn = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
+                const v4f sbn = *(const v4f*)(lsb + nbase + 16 * j + 4 * (lane >> 4));
+                v4f p[MI];
 #pragma unroll
-                for (int i = 0; i < MI; i++) {
-                    const v4f p = mfma8_group(bf, af[i]);
-                    acc[i][j] += (p * c[i]) * sbn;
-                }
+                for (int i = 0; i < MI; i++) p[i] = mfma8_group(bf, af[i]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < MI; i++) acc[i][j] += (p[i] * c[i]) * sbn;
             }
         }
     } else {
@@ -609,19 +615,54 @@ __device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm,
             af[i] = f8_frag(la, mrow, c0);
             sab[i] = e8m0(lsa[mrow]);
         }
+        if constexpr (KIND == 0) {
+            // Block kind: the next step's B pair is read from LDS while this
+            // pair multiplies, and the one block scale is read once.
+            const int col = nbase + (lane & 15);
+            const int sbk = e8m0(lsb[nbase >> 7]);
+            v8i b0 = f8_frag(lb, col, c0);
+            v8i b1 = f8_frag(lb, col + 16, c0);
 #pragma unroll
-        for (int j = 0; j < NJ; j += 2) {
-            const v8i b0 = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
-            const v8i b1 = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
-            const int s0 = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * j + (lane & 15)]);
-            const int s1 = e8m0(KIND == 0 ? lsb[nbase >> 7] : lsb[nbase + 16 * (j + 1) + (lane & 15)]);
+            for (int j = 0; j < NJ; j += 2) {
+                v8i nb0, nb1;
+                if (j + 2 < NJ) {
+                    nb0 = f8_frag(lb, col + 16 * (j + 2), c0);
+                    nb1 = f8_frag(lb, col + 16 * (j + 3), c0);
+                    // keep the reads ahead of this pair's MFMAs (the scheduler
+                    // would otherwise sink them into the registers the MFMAs free)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
 #pragma unroll
-            for (int i = 0; i < MI; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[i], acc[i][j], 0, 0, 0, s0, 0, sab[i]);
+                for (int i = 0; i < MI; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[i], acc[i][j], 0, 0, 0, sbk, 0,
+                                                                             sab[i]);
 #pragma unroll
-            for (int i = 0; i < MI; i++)
-                acc[i][j + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[i], acc[i][j + 1], 0, 0, 0, s1, 0,
-                                                                                 sab[i]);
+                for (int i = 0; i < MI; i++)
+                    acc[i][j + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[i], acc[i][j + 1], 0, 0, 0,
+                                                                                     sbk, 0, sab[i]);
+                if (j + 2 < NJ) {
+                    b0 = nb0;
+                    b1 = nb1;
+                }
+            }
+        } else {
+            // per-column scales: one read per fragment (the registers for a
+            // prefetched pair and its scales are not free here)
+#pragma unroll
+            for (int j = 0; j < NJ; j += 2) {
+                const v8i b0 = f8_frag(lb, nbase + 16 * j + (lane & 15), c0);
+                const v8i b1 = f8_frag(lb, nbase + 16 * (j + 1) + (lane & 15), c0);
+                const int s0 = e8m0(lsb[nbase + 16 * j + (lane & 15)]);
+                const int s1 = e8m0(lsb[nbase + 16 * (j + 1) + (lane & 15)]);
+#pragma unroll
+                for (int i = 0; i < MI; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[i], acc[i][j], 0, 0, 0, s0, 0,
+                                                                             sab[i]);
+#pragma unroll
+                for (int i = 0; i < MI; i++)
+                    acc[i][j + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[i], acc[i][j + 1], 0, 0, 0,
+                                                                                     s1, 0, sab[i]);
+            }
         }
         return;
     }
