@@ -13,7 +13,10 @@ step is the whole hot path over that batch, inputs already in HBM:
     Y = X W^T, block-scaled FP8 GEMM with per-128 FP32 promotion, bf16 out.
 `value` is the step's GEMM FLOPs over the step time (quantisation
 included); `roofline` covers the dominant kernel (the GEMM), its duration
-measured with HIP events on the stream it runs on.
+measured with HIP events on the stream it runs on.  Before the warmup steps
+each workload's step runs back to back for --settle seconds (untimed; the
+count is reported): after an idle gap the shader clock takes ~30-80 ms of
+sustained load to settle, and the timed steps measure the settled clock.
 
 The GEMM's accumulation mode is --accum: mfma8 (default) forms each
 128-element group partial on the FP8 matrix cores and promotes it in FP32
@@ -217,30 +220,43 @@ def parity(sample, y_bits, qx, sx, qw, sw, accum):
             "gate_passed": bool(ok and codes_ok), "gate_reason": why if codes_ok else "codes or scales differ"}
 
 
-def _sclk_file():
-    """sysfs file with the current shader clock (Hz) of the GPU torch uses,
-    or None."""
+def _clock_files():
+    """sysfs files of the GPU torch uses: the DPM clock table (its line
+    marked '*' is the current shader clock) and the power reading (uW); None
+    where absent.  With several cards visible the one on torch's PCI bus is
+    taken."""
     import torch
     try:
         props = torch.cuda.get_device_properties(0)
-        bus = getattr(props, "pci_bus_id", None)
-        dom = getattr(props, "pci_domain_id", 0) or 0
-        if bus is not None:
-            cands = glob.glob(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:00.0/hwmon/hwmon*/freq1_input")
-            if cands:
-                return cands[0]
-        cands = glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input")
-        return cands[0] if len(cands) == 1 else None
+        bus, dom = getattr(props, "pci_bus_id", None), getattr(props, "pci_domain_id", 0) or 0
+        cards = sorted(glob.glob("/sys/class/drm/card[0-9]*/device"))
+        if bus is not None and len(cards) > 1:
+            want = f"{dom:04x}:{bus:02x}:"
+            cards = [c for c in cards if os.path.basename(os.path.realpath(c)).startswith(want)] or cards
+        if not cards:
+            return None, None
+        sclk = os.path.join(cards[0], "pp_dpm_sclk")
+        power = sorted(glob.glob(os.path.join(cards[0], "hwmon", "hwmon*", "power1_input")))
+        return (sclk if os.path.exists(sclk) else None), (power[0] if power else None)
     except Exception:
-        return None
+        return None, None
+
+
+def _read_sclk_mhz(path):
+    with open(path) as f:
+        for line in f:
+            if line.rstrip().endswith("*"):
+                return float(line.split(":", 1)[1].strip().split("Mhz")[0].split("MHz")[0])
+    return None
 
 
 def measure_sclk(fn, launches=300):
-    """The shader clock while `fn` runs back to back (`launches` calls,
-    outside the timed steps): sysfs samples taken until the work drains."""
+    """The shader clock (and board power) while `fn` runs back to back
+    (`launches` calls, outside the timed steps): sysfs samples taken until
+    the work drains, the first fifth (ramp-up) dropped."""
     import torch
-    path = _sclk_file()
-    if path is None:
+    sclk_path, power_path = _clock_files()
+    if sclk_path is None:
         return None
     fn()
     torch.cuda.synchronize()
@@ -248,20 +264,28 @@ def measure_sclk(fn, launches=300):
     for _ in range(launches):
         fn()
     done.record()
-    vals = []
+    clk, pwr = [], []
     while not done.query():
         try:
-            with open(path) as f:
-                vals.append(int(f.read().strip()) / 1e6)
-        except (OSError, ValueError):
+            v = _read_sclk_mhz(sclk_path)
+            if v is not None:
+                clk.append(v)
+            if power_path:
+                with open(power_path) as f:
+                    pwr.append(int(f.read().strip()) / 1e6)
+        except (OSError, ValueError, IndexError):
             return None
         time.sleep(0.002)
     torch.cuda.synchronize()
-    if not vals:
+    if not clk:
         return None
-    v = np.array(vals[len(vals) // 5:] or vals)  # skip the ramp-up
-    return {"mean_mhz": float(v.mean()), "min_mhz": float(v.min()), "max_mhz": float(v.max()),
-            "samples": len(v), "source": f"{path} during {launches} back-to-back calls"}
+    c = np.array(clk[len(clk) // 5:] or clk)
+    out = {"mean_mhz": float(c.mean()), "min_mhz": float(c.min()), "max_mhz": float(c.max()), "samples": len(c),
+           "source": f"{sclk_path} (current level) during {launches} back-to-back calls of the timed GEMM"}
+    if pwr:
+        w = np.array(pwr[len(pwr) // 5:] or pwr)
+        out["board_power_w"] = float(w.mean())
+    return out
 
 
 def library_ceiling():
@@ -298,6 +322,27 @@ def library_ceiling():
     ms = timed(lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
     out["scaled_mm_fp8_per_tensor"] = {"ms": ms, "TFLOP/s": 2.0 * M * N * K / ms / 1e9}
     print(json.dumps({"library_ceiling": out, "shape": [M, N, K], "data": "torch.randn"}), flush=True)
+
+
+def settle(step_fns, seconds):
+    """Run the step back to back for `seconds` before the warmup steps (not
+    timed, not counted as warmup): after the GPU has idled (input generation,
+    host work) its shader clock ramps up over the first ~30-80 ms of
+    sustained load, and a 20-step timed region would otherwise measure the
+    ramp rather than the kernels.  Returns the number of steps run."""
+    import torch
+    if seconds <= 0:
+        return 0
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for fn in step_fns:
+            fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def time_steps(step_fns, steps, warmup):
@@ -448,8 +493,9 @@ def build_moe_backward(d, accum, dev):
 PEAK_UNIT = {"TFLOP/s": (PEAK_FP8_TFLOPS, "mfma"), "GB/s": (PEAK_HBM_GBPS, "hbm")}
 
 
-def run_kernels(kernels, flops, config, steps, warmup):
+def run_kernels(kernels, flops, config, steps, warmup, settle_s=0.0):
     """Time a workload's step; returns its report (the line's fields)."""
+    n_settle = settle([k[1] for k in kernels], settle_s)
     wall, per = time_steps([k[1] for k in kernels], steps, warmup)
     report = {}
     for k, ms in zip(kernels, per):
@@ -469,6 +515,7 @@ def run_kernels(kernels, flops, config, steps, warmup):
         peak, bound = PEAK_UNIT[unit]
         ach, unit2 = report[kname][unit], unit
     return {"value": flops / (wall * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": wall, "config": config,
+            "settle": {"seconds": settle_s, "steps": n_settle},
             "roofline": {"bound": bound, "achieved": ach, "peak": peak, "unit": unit2, "frac": ach / peak,
                          "traffic": None, "kernel": kname, "kernel_ms": per[dom]},
             "kernels": report}
@@ -494,7 +541,7 @@ def other_workload(name, args, data=None):
         built = build_grouped(name, d, accum, dev)
     kernels, flops, config = built
     config["accum"] = accum_name
-    rep = run_kernels(kernels, flops, config, args.steps, args.warmup)
+    rep = run_kernels(kernels, flops, config, args.steps, args.warmup, args.settle)
     del kernels, built
     torch.cuda.empty_cache()
     return rep
@@ -507,6 +554,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and the parity check")
     ap.add_argument("--no-workloads", action="store_true", help="time the dense Fprop only")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of back-to-back steps before the warmup steps, untimed (clock ramp-up)")
     ap.add_argument("--accum", choices=["mfma8", "fp32", "mfma8_pow2"], default=None,
                     help="GEMM accumulation: FP8 matrix cores (mfma8), exact group partials (fp32), or "
                          "power-of-two scales inside the FP8 MFMA (mfma8_pow2; power-of-two scales only); "
@@ -543,8 +592,8 @@ def main():
                 "warmup": args.warmup, "ms_per_step": rep["ms_per_step"], "higher_is_better": True,
                 "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
                 "data": "synthetic (seeded numpy, shapes and distributions of the workload)",
-                "config": rep["config"], "roofline": rep["roofline"], "kernels": rep["kernels"],
-                "cpu_baseline": None}
+                "config": rep["config"], "settle": rep["settle"], "roofline": rep["roofline"],
+                "kernels": rep["kernels"], "cpu_baseline": None}
         print(json.dumps(line), flush=True)
         return
 
@@ -583,10 +632,11 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    n_settle = settle([step], args.settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"settle ({n_settle} steps, {args.settle} s) and warmup done ({args.warmup} steps)")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -655,6 +705,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_FP8_TFLOPS,
                      "traffic": traffic, "kernel": kernel, "kernel_ms": gemm_ms},
+        "settle": {"seconds": args.settle, "steps": n_settle},
         "parity": None,
         "sclk": sclk,
         "gemm_modes": {
@@ -679,16 +730,16 @@ def main():
         wl = {}
         t_w = time.perf_counter()
         wl["expert_backward"] = other_workload("expert_backward", argparse.Namespace(
-            accum=None, steps=args.steps, warmup=args.warmup))
+            accum=None, steps=args.steps, warmup=args.warmup, settle=args.settle))
         log(f"expert_backward timed ({time.perf_counter() - t_w:.1f} s)")
         up = inputs.grouped_upproj()
         for name in ("grouped_upproj", "moe_backward"):
-            wl[name] = other_workload(name, argparse.Namespace(accum=None, steps=args.steps, warmup=args.warmup),
-                                      data=up)
+            wl[name] = other_workload(name, argparse.Namespace(accum=None, steps=args.steps, warmup=args.warmup,
+                                                               settle=args.settle), data=up)
             log(f"{name} timed ({time.perf_counter() - t_w:.1f} s)")
         del up
         wl["decode_grouped"] = other_workload("decode_grouped", argparse.Namespace(
-            accum=None, steps=args.steps, warmup=args.warmup))
+            accum=None, steps=args.steps, warmup=args.warmup, settle=args.settle))
         log(f"decode_grouped timed ({time.perf_counter() - t_w:.1f} s)")
         out["workloads"] = wl
 
