@@ -272,6 +272,35 @@ def _dense_fprop_reference(mode):
     return wqx, wsx, wqw, wsw, r, rabs
 
 
+@pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
+def test_group_counts_mixed_tiles(hip, orc, accum):
+    """K = 128 .. 896 (one to seven K groups: the single-group path, odd
+    counts, even counts and the steady K loop of the FP8 modes' kernels) on
+    X[4000x896] W[4200x896], a shape whose launch on a 256-CU MI355X puts
+    columns 0..2303 on 256 x 256 tiles and the rest on 256 x 128 tiles, the
+    last row and column of tiles partial.  The GEMMs run on K-prefixes of
+    the quantised operands (row strides 896); the rows of the first, a
+    middle and the last row of tiles are compared on every column."""
+    mode = 1 if accum == 2 else 0
+    M, N, KMAX = 4000, 4200, 896
+    X = inputs.random_bf16(151, (M, KMAX))
+    W = inputs.random_bf16(152, (N, KMAX), sd=0.02, outliers=False)
+    qx, sx, _, wqx, wsx, _ = quant_both(hip, orc, X, "row", mode)
+    qw, sw, _, wqw, wsw, _ = quant_both(hip, orc, W, "block", mode)
+    rows = np.r_[0:64, 1984:2048, 3904:4000]
+    for g in range(1, KMAX // 128 + 1):
+        K = 128 * g
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        hip.fp8_gemm_blockscaled(qx[:, :K], sx[:g], qw[:, :K], sw[:, :g], hip.BSCALE_BLOCK, sw.stride(0), 1, 0, d=y,
+                                 accum=accum)
+        a = np.ascontiguousarray(wqx[rows, :K])
+        sa = np.ascontiguousarray(wsx[:g, rows])
+        b = np.ascontiguousarray(wqw[:, :K])
+        sb = np.ascontiguousarray(wsw[:, :g])
+        r, rabs = full(orc, a, sa, b, sb, 0, sb.shape[1], 1)
+        check(out_f64(y)[rows], r, rabs, 0, accum, g, f"mixed tiles {M}x{N}x{K} accum={accum}")
+
+
 @ACCUMS_POW2
 def test_dense_fprop_full_size(hip, orc, accum):
     """Workload 1 at its real size (4096 x 18432 x 7168, bf16 out) in the
