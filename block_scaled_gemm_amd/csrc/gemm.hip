@@ -123,6 +123,23 @@ struct Shape<2> {
     }
 };
 
+//  Shape 5: shape 2's 128 x 128 tile and wave grid with two stages
+//    (66 KB, which the 128 x 128 fp32 output image also fits): the
+//    K-grouped Wgrad, whose experts hold one or two K groups and whose
+//    cost is the fp32 output, runs two workgroups per CU with it, so one
+//    workgroup's stores overlap the other's loads and MFMAs.
+template <>
+struct Shape<5> {
+    static constexpr int BM = 128, BN = 128;
+    static constexpr int WM = 32, WN = 64;
+    static constexpr int STAGES = 2;
+    // SIMD s holds waves s and s + 4: one m-slot, both n-slots
+    __device__ static void wave_grid(int wave, int& wm, int& wn) {
+        wm = wave & 3;
+        wn = wave >> 2;
+    }
+};
+
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
 template <int SH>
@@ -1123,6 +1140,44 @@ __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t t
     }
 }
 
+// The FP8 modes' K-grouped Wgrad on shape 5, two workgroups per CU
+// (128 VGPRs per lane); work split as kgrouped_kernel.
+template <int ACC, int OUT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void kgrouped2_kernel(
+    GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<5>::BYTES];
+    // workgroup = (expert, strip of KSTRIP m-tiles, n-tile); consecutive
+    // workgroups take consecutive n-tiles of the same rows, so the tiles in
+    // flight together write adjacent 512 B pieces of the same output rows
+    const int64_t strips = (tiles_m + KSTRIP - 1) / KSTRIP;
+    const int64_t per = tiles_n * strips;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t e = wid / per;
+    const int64_t tn = (wid % per) % tiles_n, strip = (wid % per) / tiles_n;
+    const int64_t g0 = expert_first_group(p.offsets, e);
+    const int64_t g1 = g0 + ((int64_t)p.offsets[e + 1] - p.offsets[e] + 127) / 128;
+
+    Tile T;
+    T.n0 = tn * Shape<5>::BN;
+    T.m_end = p.M;
+    T.n_end = p.N;
+    T.a = p.a;
+    T.lda = p.lda;
+    T.sa = p.sa;
+    T.ldsa = p.ldsa;
+    T.b = p.b;
+    T.ldb = p.ldb;
+    T.sb = p.sb;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = 0;
+    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT ? 4 : 2);
+    const int64_t tm_end = (strip + 1) * KSTRIP < tiles_m ? (strip + 1) * KSTRIP : tiles_m;
+    for (int64_t tm = strip * KSTRIP; tm < tm_end; tm++) {
+        T.m0 = tm * Shape<5>::BM;
+        run_tile<ACC, 5, 1, OUT>(T, g0, g1, d, p.ldd, smem);
+    }
+}
+
 // Sum split-K partials in split order and convert.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
@@ -1297,6 +1352,15 @@ static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
 
 template <int ACC>
 static hipError_t launch_kgrouped_acc(const GemmArgs& g, hipStream_t st) {
+    if constexpr (ACC != 0) {
+        const int64_t tiles_m = (g.M + 127) / 128, tiles_n = (g.N + 127) / 128;
+        const dim3 grid((unsigned)(tiles_n * ((tiles_m + KSTRIP - 1) / KSTRIP) * g.G));
+        if (g.out_f32)
+            hipLaunchKernelGGL((kgrouped2_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+        else
+            hipLaunchKernelGGL((kgrouped2_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+        return hipGetLastError();
+    }
     const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
     const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     const dim3 grid((unsigned)(tiles_m * ((tiles_n + KSTRIP - 1) / KSTRIP) * g.G));
