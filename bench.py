@@ -66,10 +66,17 @@ sys.path.insert(0, ROOT)
 M, N, K = 4096, 18432, 7168
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_fprop_traffic.txt")
+# per-launch HBM traffic and counters of every workload kernel, written by
+# --summarize-profile from the rocprofv3 passes over --profile-kernels
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "kernels_per_launch.md")
+PROFILE_SOURCES = ["block_scaled_gemm_amd/csrc/gemm.hip", "block_scaled_gemm_amd/csrc/quant.hip",
+                   "block_scaled_gemm_amd/csrc/device.h", "block_scaled_gemm_amd/csrc/kernels.h",
+                   "block_scaled_gemm_amd/csrc/api.cpp"]
+PROFILE_CALLS = 3
+# the dense Fprop GEMM of the default line, as --profile-kernels labels it
+DENSE_GEMM_LABEL = "gemm 4096x18432x7168 (FP32 scales, FP8 matrix cores)"
 # the kernel one dense-Fprop GEMM call launches, per accumulation mode
 GEMM_KERNEL = {"mfma8": "gemm_wide_kernel<1, 0, 0>", "fp32": "gemm_kernel<0, 0, 0, 0, false>"}
-KERNEL_SOURCES = ["block_scaled_gemm_amd/csrc/gemm.hip", "block_scaled_gemm_amd/csrc/device.h"]
 METRIC = "block-scaled FP8 GEMM TFLOP/s (% MFMA peak); quantize GB/s (% HBM peak)"
 
 
@@ -95,22 +102,30 @@ def quant_bytes_block(rows, cols):
     return rows * cols * 3 + ((rows + 127) // 128) * (cols // 128) * 4
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source.
-    The summary is text: `key: value` lines."""
+def read_profile_summary(path=None):
+    """{label: HBM bytes per launch} from the committed summary, or {} when it
+    is absent or was taken on other kernel sources.  Machine-readable lines
+    of the summary: `source_hash: H` and `traffic | <label> | <bytes>`."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        with open(path or PROFILE_SUMMARY) as f:
+            lines = f.read().splitlines()
     except OSError:
-        return None
-    kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_hash") != source_hash(KERNEL_SOURCES) or kv.get("kernel") != kernel:
-        return None
-    try:
-        return float(kv["bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    h = next((ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("source_hash:")), None)
+    if h != source_hash(PROFILE_SOURCES):
+        return {}
+    out = {}
+    for ln in lines:
+        if ln.startswith("traffic | "):
+            _, label, b = [x.strip() for x in ln.split("|")]
+            out[label] = float(b)
+    return out
+
+
+def measured_traffic(label):
+    """HBM bytes per launch of the workload kernel `label` (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None."""
+    return read_profile_summary().get(label)
 
 
 def traffic_probe():
@@ -517,8 +532,227 @@ def run_kernels(kernels, flops, config, steps, warmup, settle_s=0.0):
     return {"value": flops / (wall * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": wall, "config": config,
             "settle": {"seconds": settle_s, "steps": n_settle},
             "roofline": {"bound": bound, "achieved": ach, "peak": peak, "unit": unit2, "frac": ach / peak,
-                         "traffic": None, "kernel": kname, "kernel_ms": per[dom]},
+                         "traffic": measured_traffic(kname), "kernel": kname, "kernel_ms": per[dom]},
             "kernels": report}
+
+
+def build_dense(d, dev):
+    """The dense Fprop's kernels for --profile-kernels: the default line's
+    quantisers and GEMM, plus the GEMM in the exact mode and in the
+    power-of-two mode (on power-of-two quantisations)."""
+    import torch
+    import block_scaled_gemm_amd as bs
+    X, W = _to_bf16(d["X"], dev), _to_bf16(d["W"], dev)
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_FP32, q=qx, s=sx)
+    bs.fp8_quant_block(W, bs.SCALE_FP32, q=qw, s=sw)
+    qx2, sx2 = bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_POW2)
+    qw2, sw2, _ = bs.fp8_quant_block(W, bs.SCALE_POW2)
+    # algorithmic bytes: both operands' codes and scales once, the bf16 output once
+    ideal = M * K + N * K + (K // 128) * M * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
+    gemm = lambda a, sa, b, sb, acc: (lambda: bs.fp8_gemm_blockscaled(a, sa, b, sb, bs.BSCALE_BLOCK, K // 128, 1,
+                                                                      bs.OUT_BF16, d=y, accum=acc))
+    F = 2.0 * M * N * K / 1e3
+    return [
+        (f"quant_tile X[{M}x{K}]", lambda: bs.fp8_quant_tile(X, bs.AXIS_ROW, bs.SCALE_FP32, q=qx, s=sx),
+         quant_bytes_row(M, K), "GB/s"),
+        (f"quant_block W[{N}x{K}]", lambda: bs.fp8_quant_block(W, bs.SCALE_FP32, q=qw, s=sw),
+         quant_bytes_block(N, K), "GB/s"),
+        (DENSE_GEMM_LABEL, gemm(qx, sx, qw, sw, bs.ACCUM_MFMA8), F, "TFLOP/s", ideal),
+        (f"gemm {M}x{N}x{K} (exact group partials, f16 matrix cores)", gemm(qx, sx, qw, sw, bs.ACCUM_FP32), F,
+         "TFLOP/s", ideal),
+        (f"gemm {M}x{N}x{K} (power-of-two scales inside the FP8 MFMA)", gemm(qx2, sx2, qw2, sw2,
+                                                                            bs.ACCUM_MFMA8_POW2), F, "TFLOP/s",
+         ideal),
+    ]
+
+
+def profile_kernels():
+    """Every workload kernel on its own: a marker dispatch (torch's spin
+    kernel), then PROFILE_CALLS launches of the kernel, then a
+    synchronisation -- the layout --summarize-profile splits rocprofv3's
+    per-dispatch records by.  Prints the manifest (labels in launch order,
+    algorithmic work) as one JSON line."""
+    import torch
+    from block_scaled_gemm_amd import inputs
+    import block_scaled_gemm_amd as bs
+    if not hasattr(torch.cuda, "_sleep"):
+        raise RuntimeError("torch.cuda._sleep (the marker dispatch) is missing")
+    dev = torch.device("cuda:0")
+    manifest = []
+
+    def run(workload, kernels):
+        for k in kernels:  # warm, before any marker
+            k[1]()
+        torch.cuda.synchronize()
+        for k in kernels:
+            torch.cuda._sleep(1000)
+            for _ in range(PROFILE_CALLS):
+                k[1]()
+            torch.cuda.synchronize()
+            manifest.append({"workload": workload, "label": k[0], "calls": PROFILE_CALLS, "work": k[2],
+                             "unit": k[3], "bytes": k[4] if len(k) > 4 else (k[2] if k[3] == "GB/s" else None)})
+        log(f"profiled {workload} ({len(kernels)} kernels)")
+
+    run("dense_fprop", build_dense(inputs.dense_fprop(), dev))
+    torch.cuda.empty_cache()
+    run("expert_backward", build_expert_backward(inputs.expert_backward(), bs.ACCUM_MFMA8, dev)[0])
+    torch.cuda.empty_cache()
+    up = inputs.grouped_upproj()
+    run("grouped_upproj", build_grouped("grouped_upproj", up, bs.ACCUM_MFMA8_POW2, dev)[0])
+    torch.cuda.empty_cache()
+    run("moe_backward", build_moe_backward(up, bs.ACCUM_MFMA8, dev)[0])
+    del up
+    torch.cuda.empty_cache()
+    run("decode_grouped", build_grouped("decode_grouped", inputs.decode_grouped(), bs.ACCUM_MFMA8, dev)[0])
+    torch.cuda._sleep(1000)  # closes the last segment
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_manifest": manifest, "source_hash": source_hash(PROFILE_SOURCES)}), flush=True)
+
+
+MARKER = "spin_kernel"  # torch.cuda._sleep's kernel
+_PK = "python3 /root/repo/bench.py --profile-kernels"
+PROFILE_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    f"rocprofv3 --kernel-trace --output-format csv -d <out>/trace -o p -- {_PK} > <out>/manifest.json",
+    f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o p -- {_PK}",
+    f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o p -- {_PK}",
+    "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU GRBM_GUI_ACTIVE --output-format csv "
+    f"-d <out>/sq -o p -- {_PK}",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/probe_fetch -o p -- "
+    "python3 /root/repo/bench.py --traffic-probe",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/probe_write -o p -- "
+    "python3 /root/repo/bench.py --traffic-probe",
+    "python3 /root/repo/bench.py --summarize-profile <out> <out>/manifest.json",
+]
+
+
+def _csv_rows(root, suffix):
+    import csv
+    rows = []
+    for dirpath, _, names in sorted(os.walk(root)):
+        for n in sorted(names):
+            if n.endswith(suffix):
+                with open(os.path.join(dirpath, n), newline="") as f:
+                    rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name):
+    import re
+    n = re.sub(r"^void ", "", name)
+    n = n.replace("fp8bs::", "")
+    return re.sub(r"\(.*$", "", n).strip()
+
+
+def _dispatches(root, suffix):
+    """[(dispatch id, kernel name, {counter: value} or duration ns)] in
+    dispatch order from one rocprofv3 pass."""
+    rows = _csv_rows(root, suffix)
+    if not rows:
+        raise RuntimeError(f"no *{suffix} under {root}")
+    key = "Dispatch_Id" if "Dispatch_Id" in rows[0] else "Correlation_Id"
+    by = {}
+    for r in rows:
+        i = int(r[key])
+        name = r["Kernel_Name"]
+        if "Counter_Name" in r:
+            e = by.setdefault(i, (name, {}))
+            e[1][r["Counter_Name"]] = e[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        else:
+            by[i] = (name, int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return [(i, by[i][0], by[i][1]) for i in sorted(by)]
+
+
+def _segments(disp, n):
+    """Split a dispatch list at the marker dispatches into the n segments
+    that follow the first n markers."""
+    marks = [k for k, (_, name, _) in enumerate(disp) if MARKER in name]
+    if len(marks) < n + 1:
+        names = sorted({_short(x[1]) for x in disp})[:20]
+        raise RuntimeError(f"{len(marks)} marker dispatches for {n} kernels; kernels seen: {names}")
+    return [[x for x in disp[marks[k] + 1:marks[k + 1]]] for k in range(n)]
+
+
+def _probe_factor(root, counter, true_bytes):
+    """Counter bytes per true byte for the copy probe (the largest dispatch
+    of the probe run)."""
+    disp = _dispatches(root, "counter_collection.csv")
+    kib = max(v.get(counter, 0.0) for _, _, v in disp)
+    return kib * 1024.0 / true_bytes
+
+
+def summarize_profile(root, manifest_path, out_path, command):
+    """The per-kernel summary from the rocprofv3 passes under `root`
+    (subfolders trace/, fetch/, write/, sq/, probe_fetch/, probe_write/) and
+    the manifest line that --profile-kernels printed; written as text with
+    the machine-readable `traffic | label | bytes` lines."""
+    with open(manifest_path) as f:
+        man = next(json.loads(ln) for ln in f if ln.startswith("{") and "profile_manifest" in ln)
+    entries = man["profile_manifest"]
+    n = len(entries)
+    seg = {}
+    seg["trace"] = _segments(_dispatches(os.path.join(root, "trace"), "kernel_trace.csv"), n)
+    for p in ("fetch", "write", "sq"):
+        seg[p] = _segments(_dispatches(os.path.join(root, p), "counter_collection.csv"), n)
+    probe = 1 << 30  # torch.neg over 2^28 fp32: 1 GiB read, 1 GiB written
+    ff = _probe_factor(os.path.join(root, "probe_fetch"), "FETCH_SIZE", probe)
+    wf = _probe_factor(os.path.join(root, "probe_write"), "WRITE_SIZE", probe)
+    lines = [
+        "# Per-launch time, HBM traffic and matrix-core / VALU activity of every workload kernel (one MI355X)",
+        "",
+        "Commands (each kernel launched on its own after a marker dispatch; one rocprofv3 pass per row):",
+        "",
+    ]
+    lines += ["    " + c for c in command]
+    lines += [
+        "",
+        f"Counter scaling from the copy probe (torch.neg, 1 GiB read + 1 GiB written): FETCH_SIZE {ff:.4f} "
+        f"counter bytes per byte read, WRITE_SIZE {wf:.4f} per byte written; traffic = FETCH/{ff:.4f} + "
+        f"WRITE/{wf:.4f}.  Clock = (GRBM_GUI_ACTIVE / 8 XCDs) / duration; MFMA busy = "
+        "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); VALU = 4 x SQ_INSTS_VALU / (1024 x cycles).  "
+        "Short kernels (< 50 us) get an overstated clock window, so their busy fractions are left out.",
+        "",
+        "| workload | kernel (label) | HIP kernels | us/launch | MB read | MB written | traffic / algorithmic | "
+        "achieved | MFMA busy | VALU | clock GHz |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    machine = []
+    for k, e in enumerate(entries):
+        calls = e["calls"]
+        names = sorted({_short(x[1]) for x in seg["trace"][k]})
+        us = sum(x[2] for x in seg["trace"][k]) / calls / 1e3
+        rd = sum(x[2].get("FETCH_SIZE", 0.0) for x in seg["fetch"][k]) * 1024.0 / ff / calls
+        wr = sum(x[2].get("WRITE_SIZE", 0.0) for x in seg["write"][k]) * 1024.0 / wf / calls
+        sq = {}
+        for x in seg["sq"][k]:
+            for c, v in x[2].items():
+                sq[c] = sq.get(c, 0.0) + v / calls
+        alg = e.get("bytes")
+        ratio = f"{(rd + wr) / alg:.2f}" if alg else "-"
+        if e["unit"] == "GB/s":
+            ach = f"{e['work'] / (us * 1e-6) / 1e9:.0f} GB/s"
+        else:
+            ach = f"{e['work'] * 1e3 / (us * 1e-6) / 1e12:.0f} TFLOP/s"
+        cyc = sq.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        if us >= 50 and cyc > 0:
+            ghz = cyc / (us * 1e3)
+            mfma = f"{100 * sq.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / (1024 * cyc):.1f}%"
+            valu = f"{100 * 4 * sq.get('SQ_INSTS_VALU', 0.0) / (1024 * cyc):.1f}%"
+            clk = f"{ghz:.2f}"
+        else:
+            mfma = valu = clk = "-"
+        lines.append(f"| {e['workload']} | {e['label']} | {', '.join(f'`{x}`' for x in names)} | {us:.1f} | "
+                     f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {ratio} | {ach} | {mfma} | {valu} | {clk} |")
+        machine.append(f"traffic | {e['label']} | {rd + wr:.0f}")
+    lines += ["", "Machine-readable (bench.py reads these while the kernel sources are unchanged):", "",
+              f"source_hash: {man['source_hash']}"] + machine
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def other_workload(name, args, data=None):
@@ -562,6 +796,10 @@ def main():
                          "default: mfma8_pow2 for grouped_upproj, mfma8 elsewhere")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only a plain copy of known size (counter scaling)")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="launch every workload kernel on its own after a marker dispatch (for rocprofv3 passes)")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("DIR", "MANIFEST"),
+                    help="write the per-kernel summary from rocprofv3 passes over --profile-kernels")
     ap.add_argument("--library-ceiling", action="store_true",
                     help="time the vendor GEMMs on the dense shape (context only)")
     ap.add_argument("--workload", default="dense_fprop",
@@ -582,6 +820,13 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.profile_kernels:
+        profile_kernels()
+        return
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile[0], args.summarize_profile[1], PROFILE_SUMMARY,
+                          PROFILE_COMMANDS)
         return
     if args.library_ceiling:
         library_ceiling()
@@ -684,7 +929,8 @@ def main():
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     bx, bw = quant_bytes_row(M, K), quant_bytes_block(N, K)
-    traffic = measured_traffic(kernel)
+    traffic = measured_traffic(DENSE_GEMM_LABEL if accum_name == "mfma8" else
+                               f"gemm {M}x{N}x{K} (exact group partials, f16 matrix cores)")
     flops_tf = lambda ms: flops / (ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,

@@ -1,5 +1,6 @@
 """Host logic of bench.py (no GPU): the one-GPU guard, the mode guards, the
 algorithmic byte counts and the traffic summary's source check."""
+import json
 import os
 import subprocess
 import sys
@@ -42,19 +43,94 @@ def test_algorithmic_bytes_of_the_quantisers():
 
 
 def test_traffic_is_used_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
-    kernel = bench.GEMM_KERNEL["mfma8"]
-    good = tmp_path / "traffic.txt"
-    good.write_text(f"# comment: with a colon\nkernel: {kernel}\nsource_hash: {bench.source_hash(bench.KERNEL_SOURCES)}\n"
-                    "bytes_per_launch: 1234\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
-    assert bench.measured_traffic(kernel) == 1234.0
-    assert bench.measured_traffic("some_other_kernel<0>") is None
-    stale = tmp_path / "stale.txt"
-    stale.write_text(f"kernel: {kernel}\nsource_hash: 0000000000000000\nbytes_per_launch: 1234\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
-    assert bench.measured_traffic(kernel) is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
-    assert bench.measured_traffic(kernel) is None
+    label = bench.DENSE_GEMM_LABEL
+    good = tmp_path / "summary.md"
+    good.write_text(f"# title: with a colon\nsource_hash: {bench.source_hash(bench.PROFILE_SOURCES)}\n"
+                    f"traffic | {label} | 1234\ntraffic | quant_tile X[4096x7168] | 99\n")
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(good))
+    assert bench.measured_traffic(label) == 1234.0
+    assert bench.measured_traffic("quant_tile X[4096x7168]") == 99.0
+    assert bench.measured_traffic("some other kernel") is None
+    stale = tmp_path / "stale.md"
+    stale.write_text(f"source_hash: 0000000000000000\ntraffic | {label} | 1234\n")
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(stale))
+    assert bench.measured_traffic(label) is None
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(tmp_path / "absent.md"))
+    assert bench.measured_traffic(label) is None
+
+
+TRACE_HEAD = "Kind,Agent_Id,Queue_Id,Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+PMC_HEAD = "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+SPIN = "at::cuda::(anonymous namespace)::spin_kernel(long)"
+
+
+def _write_pass(path, rows, pmc):
+    path.mkdir(parents=True)
+    with open(path / ("p_counter_collection.csv" if pmc else "p_kernel_trace.csv"), "w") as f:
+        f.write(PMC_HEAD if pmc else TRACE_HEAD)
+        for r in rows:
+            f.write(",".join(f'"{x}"' if isinstance(x, str) and "," in x else str(x) for x in r) + "\n")
+
+
+def test_profile_summary_splits_dispatches_at_the_markers(tmp_path, monkeypatch):
+    """Two labels, 3 launches each; label A launches one kernel per call,
+    label B two (a GEMM and its reduction).  Dispatches before the first
+    marker (warm-up) and torch kernels outside the segments are ignored;
+    counters are divided per launch and scaled by the copy probe."""
+    calls = bench.PROFILE_CALLS
+    seq = [("void fp8bs::warm_kernel<1>(fp8bs::GemmArgs)", 999)]  # before the first marker
+    seq.append((SPIN, 1))
+    seq += [("void fp8bs::quant_row_kernel<false, 4>(int)", 10)] * calls
+    seq.append((SPIN, 1))
+    seq += [("void fp8bs::gemm_kernel<1, 0, 1, 1, true>(fp8bs::GemmArgs, long, long)", 100),
+            ("void fp8bs::splitk_reduce_kernel<1>(float const*)", 20)] * calls
+    seq.append((SPIN, 1))
+    trace, fetch, write, sq = [], [], [], []
+    for i, (name, w) in enumerate(seq):
+        did = 100 + i
+        trace.append(("KERNEL_DISPATCH", 1, 1, did, name, 1000 * i, 1000 * i + 1000 * w))  # w us
+        fetch.append((did, name, 64, "FETCH_SIZE", 2.0 * w))     # KiB, probe factor 2
+        write.append((did, name, 64, "WRITE_SIZE", 1.0 * w))
+        sq.append((did, name, 64, "GRBM_GUI_ACTIVE", 8 * 2000.0 * w))  # 2 GHz over w us
+        sq.append((did, name, 64, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000.0 * w))  # half busy
+        sq.append((did, name, 64, "SQ_INSTS_VALU", 0.0))
+    root = tmp_path / "prof"
+    _write_pass(root / "trace", trace, False)
+    _write_pass(root / "fetch", fetch, True)
+    _write_pass(root / "write", write, True)
+    _write_pass(root / "sq", sq, True)
+    gib = float(1 << 30)
+    _write_pass(root / "probe_fetch", [(1, "neg_kernel", 64, "FETCH_SIZE", 2 * gib / 1024)], True)
+    _write_pass(root / "probe_write", [(1, "neg_kernel", 64, "WRITE_SIZE", gib / 1024)], True)
+    man = tmp_path / "manifest.json"
+    man.write_text("[bench] log line\n" + json.dumps({"profile_manifest": [
+        {"workload": "w", "label": "A", "calls": calls, "work": 20480.0, "unit": "GB/s", "bytes": 20480.0},
+        {"workload": "w", "label": "B", "calls": calls, "work": 1.0, "unit": "TFLOP/s", "bytes": None}],
+        "source_hash": bench.source_hash(bench.PROFILE_SOURCES)}) + "\n")
+    out = tmp_path / "summary.md"
+    bench.summarize_profile(str(root), str(man), str(out), ["cmd one", "cmd two"])
+    text = out.read_text()
+    assert "    cmd one" in text and "`quant_row_kernel<false, 4>`" in text
+    assert "`gemm_kernel<1, 0, 1, 1, true>`, `splitk_reduce_kernel<1>`" in text
+    got = bench.read_profile_summary(str(out))
+    # A: a 20 KiB FETCH_SIZE (probe factor 2: 10 KiB read) + 10 KiB written per launch
+    assert got["A"] == pytest.approx(10 * 1024 + 10 * 1024)
+    # B: (200 + 40) KiB FETCH_SIZE / 2 + (100 + 20) KiB written per launch
+    assert got["B"] == pytest.approx(120 * 1024 + 120 * 1024)
+    row_b = next(ln for ln in text.splitlines() if ln.startswith("| w | B |"))
+    cells = [c.strip() for c in row_b.split("|")]
+    assert cells[4] == "120.0"            # us per launch
+    assert cells[9] == "50.0%" and cells[11] == "2.00"  # MFMA busy, clock
+    row_a = next(ln for ln in text.splitlines() if ln.startswith("| w | A |"))
+    assert row_a.split("|")[7].strip() == "1.00"  # traffic equals the algorithmic bytes
+
+
+def test_profile_summary_needs_a_marker_per_kernel(tmp_path):
+    root = tmp_path / "prof"
+    _write_pass(root / "trace", [("KERNEL_DISPATCH", 1, 1, 1, SPIN, 0, 10),
+                                 ("KERNEL_DISPATCH", 1, 1, 2, "k", 10, 20)], False)
+    with pytest.raises(RuntimeError, match="marker"):
+        bench._segments(bench._dispatches(str(root / "trace"), "kernel_trace.csv"), 1)
 
 
 def _tiny_sample():
