@@ -573,10 +573,12 @@ def build_dense(d, dev):
 
 def profile_kernels():
     """Every workload kernel on its own: a marker dispatch (torch's spin
-    kernel), then PROFILE_CALLS launches of the kernel, then a
+    kernel), PROFILE_CALLS launches of the kernel, a second marker, then a
     synchronisation -- the layout --summarize-profile splits rocprofv3's
-    per-dispatch records by.  Prints the manifest (labels in launch order,
-    algorithmic work) as one JSON line."""
+    per-dispatch records by (whatever runs between a closing marker and the
+    next opening one, such as building the next workload's inputs, is not
+    counted).  Prints the manifest (labels in launch order, algorithmic
+    work) as one JSON line."""
     import torch
     from block_scaled_gemm_amd import inputs
     import block_scaled_gemm_amd as bs
@@ -590,9 +592,10 @@ def profile_kernels():
             k[1]()
         torch.cuda.synchronize()
         for k in kernels:
-            torch.cuda._sleep(1000)
+            torch.cuda._sleep(1000)  # opens the kernel's segment
             for _ in range(PROFILE_CALLS):
                 k[1]()
+            torch.cuda._sleep(1000)  # closes it
             torch.cuda.synchronize()
             manifest.append({"workload": workload, "label": k[0], "calls": PROFILE_CALLS, "work": k[2],
                              "unit": k[3], "bytes": k[4] if len(k) > 4 else (k[2] if k[3] == "GB/s" else None)})
@@ -609,8 +612,6 @@ def profile_kernels():
     del up
     torch.cuda.empty_cache()
     run("decode_grouped", build_grouped("decode_grouped", inputs.decode_grouped(), bs.ACCUM_MFMA8, dev)[0])
-    torch.cuda._sleep(1000)  # closes the last segment
-    torch.cuda.synchronize()
     print(json.dumps({"profile_manifest": manifest, "source_hash": source_hash(PROFILE_SOURCES)}), flush=True)
 
 
@@ -669,13 +670,13 @@ def _dispatches(root, suffix):
 
 
 def _segments(disp, n):
-    """Split a dispatch list at the marker dispatches into the n segments
-    that follow the first n markers."""
+    """The dispatches between the opening and the closing marker of each of
+    the n kernels (markers come in pairs)."""
     marks = [k for k, (_, name, _) in enumerate(disp) if MARKER in name]
-    if len(marks) < n + 1:
+    if len(marks) != 2 * n:
         names = sorted({_short(x[1]) for x in disp})[:20]
-        raise RuntimeError(f"{len(marks)} marker dispatches for {n} kernels; kernels seen: {names}")
-    return [[x for x in disp[marks[k] + 1:marks[k + 1]]] for k in range(n)]
+        raise RuntimeError(f"{len(marks)} marker dispatches for {n} kernels (two each); kernels seen: {names}")
+    return [disp[marks[2 * k] + 1:marks[2 * k + 1]] for k in range(n)]
 
 
 def _probe_factor(root, counter, true_bytes):

@@ -82,6 +82,8 @@ def test_profile_summary_splits_dispatches_at_the_markers(tmp_path, monkeypatch)
     seq.append((SPIN, 1))
     seq += [("void fp8bs::quant_row_kernel<false, 4>(int)", 10)] * calls
     seq.append((SPIN, 1))
+    seq.append(("void fp8bs::setup_kernel(int)", 777))  # between two kernels' segments: not counted
+    seq.append((SPIN, 1))
     seq += [("void fp8bs::gemm_kernel<1, 0, 1, 1, true>(fp8bs::GemmArgs, long, long)", 100),
             ("void fp8bs::splitk_reduce_kernel<1>(float const*)", 20)] * calls
     seq.append((SPIN, 1))
@@ -128,9 +130,10 @@ def test_profile_summary_splits_dispatches_at_the_markers(tmp_path, monkeypatch)
 def test_profile_summary_needs_a_marker_per_kernel(tmp_path):
     root = tmp_path / "prof"
     _write_pass(root / "trace", [("KERNEL_DISPATCH", 1, 1, 1, SPIN, 0, 10),
-                                 ("KERNEL_DISPATCH", 1, 1, 2, "k", 10, 20)], False)
+                                 ("KERNEL_DISPATCH", 1, 1, 2, "k", 10, 20),
+                                 ("KERNEL_DISPATCH", 1, 1, 3, SPIN, 20, 30)], False)
     with pytest.raises(RuntimeError, match="marker"):
-        bench._segments(bench._dispatches(str(root / "trace"), "kernel_trace.csv"), 1)
+        bench._segments(bench._dispatches(str(root / "trace"), "kernel_trace.csv"), 2)
 
 
 def _tiny_sample():
