@@ -128,29 +128,44 @@ __device__ __forceinline__ uint4 load_chunk_masked(const uint16_t* __restrict__ 
 // One 128x1 group per column for 64 columns: source rows xr[i*ldx], i < nrows
 // (rows nrows..127 read as zero: they add nothing to the amax and encode to
 // zero codes), codes to qg[col*ldq + i], scale to sg[col].
+// Loads of one 128-row group x 64 columns: lane (chunk, p) of wave w holds
+// the 8-column chunk of rows w*32 + 16*it + 2p and the row after it.
+struct ColLoads {
+    uint4 lo[2], hi[2];
+};
+
+__device__ __forceinline__ void col_group_load(const uint16_t* __restrict__ xr, int nrows, int64_t cols, int64_t ldx,
+                                               int64_t c0, ColLoads& L) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int chunk = lane >> 3, p = lane & 7;
+    const int64_t col = c0 + chunk * 8;
+    const bool ok = col < cols;
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const int r = wave * 32 + it * 16 + 2 * p;
+        const uint16_t* src = xr + r * ldx + col;
+        L.lo[it] = ok && r < nrows ? load_chunk_masked(src, col, cols) : make_uint4(0, 0, 0, 0);
+        L.hi[it] = ok && r + 1 < nrows ? load_chunk_masked(src + ldx, col, cols) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// The loaded group through the LDS tile (paired-row dwords, column-major),
+// then each DPP row quantises one column's 128 values and stores them as
+// one 128 B run.
 template <bool POW2>
-__device__ __forceinline__ void col_group_tile(const uint16_t* __restrict__ xr, int nrows, int64_t cols,
-                                               int64_t ldx, int64_t c0, uint8_t* __restrict__ qg, int64_t ldq,
-                                               float* __restrict__ sg, uint32_t* tile) {
+__device__ __forceinline__ void col_group_finish(const ColLoads& L, int64_t cols, int64_t c0,
+                                                 uint8_t* __restrict__ qg, int64_t ldq, float* __restrict__ sg,
+                                                 uint32_t* tile) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     {
         const int chunk = lane >> 3, p = lane & 7;
-        const int64_t col = c0 + chunk * 8;
-        const bool ok = col < cols;
-        uint4 lo[2], hi[2];
-#pragma unroll
-        for (int it = 0; it < 2; it++) {
-            const int r = wave * 32 + it * 16 + 2 * p;
-            const uint16_t* src = xr + r * ldx + col;
-            lo[it] = ok && r < nrows ? load_chunk_masked(src, col, cols) : make_uint4(0, 0, 0, 0);
-            hi[it] = ok && r + 1 < nrows ? load_chunk_masked(src + ldx, col, cols) : make_uint4(0, 0, 0, 0);
-        }
 #pragma unroll
         for (int it = 0; it < 2; it++) {
             const int rp = wave * 16 + it * 8 + p;
-            const uint32_t a[4] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w};
-            const uint32_t b[4] = {hi[it].x, hi[it].y, hi[it].z, hi[it].w};
+            const uint32_t a[4] = {L.lo[it].x, L.lo[it].y, L.lo[it].z, L.lo[it].w};
+            const uint32_t b[4] = {L.hi[it].x, L.hi[it].y, L.hi[it].z, L.hi[it].w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int c = chunk * 8 + 2 * j;
@@ -177,6 +192,15 @@ __device__ __forceinline__ void col_group_tile(const uint16_t* __restrict__ xr, 
 }
 
 template <bool POW2>
+__device__ __forceinline__ void col_group_tile(const uint16_t* __restrict__ xr, int nrows, int64_t cols,
+                                               int64_t ldx, int64_t c0, uint8_t* __restrict__ qg, int64_t ldq,
+                                               float* __restrict__ sg, uint32_t* tile) {
+    ColLoads L;
+    col_group_load(xr, nrows, cols, ldx, c0, L);
+    col_group_finish<POW2>(L, cols, c0, qg, ldq, sg, tile);
+}
+
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ q, int64_t ldq,
@@ -199,69 +223,49 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
 // offsets[e+1]-1).  Every expert is cut into 128-token groups from its first
 // token, the last one possibly partial, and the groups are numbered
 // consecutively on a padded token axis (expert e starts at 128 * the number of
-// groups before it).  Workgroup (padded group p, 64 columns) finds its
-// expert with a block-wide prefix sum of the experts' group counts, then
-// quantises like quant_col_kernel with the rows past the expert's end read
-// as zero -- its padding codes come out zero.
-
-// Expert owning padded group p and the group's index inside it; e = -1 when
-// p is past the last group.  Every thread gets the result.
-__device__ __forceinline__ void find_expert_group(const int32_t* __restrict__ offsets, int G, int64_t p, int& e_out,
-                                                  int64_t& j_out) {
-    __shared__ int64_t wsum[4];
-    __shared__ int s_e;
-    __shared__ int64_t s_j;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    if (t == 0) s_e = -1;
-    int64_t base = 0;
-    for (int e0 = 0; e0 < G; e0 += 256) {
-        const int e = e0 + t;
-        const int64_t cnt = e < G ? ((int64_t)offsets[e + 1] - offsets[e] + 127) / 128 : 0;
-        int64_t incl = cnt;  // inclusive scan within the wave
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int64_t y = __shfl_up(incl, d);
-            if (lane >= d) incl += y;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        int64_t before = base;
-        for (int w = 0; w < wave; w++) before += wsum[w];
-        const int64_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        const int64_t first = before + incl - cnt;
-        if (cnt > 0 && p >= first && p < first + cnt) {
-            s_e = e;
-            s_j = p - first;
-        }
-        base += total;
-        __syncthreads();
-    }
-    __syncthreads();
-    e_out = s_e;
-    j_out = s_e >= 0 ? s_j : 0;
-}
-
+// groups before it).  Each group is quantised like quant_col_kernel with
+// the rows past the expert's end read as zero -- its padding codes come out
+// zero.
+//
+// Workgroup (expert e, 64 columns) quantises the expert's groups in turn.
+// Its first group's loads depend only on offsets[e] and are issued first;
+// the expert's place on the padded axis (the groups of the experts before
+// it), which only the stores need, is summed while they are in flight.
+// Consecutive workgroups take consecutive experts of one column tile, whose
+// groups follow one another on the padded axis.
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_grouped_col_kernel(const uint16_t* __restrict__ x, int64_t cols,
                                                                 int64_t ldx, int G,
                                                                 const int32_t* __restrict__ offsets,
                                                                 uint8_t* __restrict__ q, int64_t ldq,
-                                                                float* __restrict__ s, int64_t lds,
-                                                                int64_t col_tiles) {
+                                                                float* __restrict__ s, int64_t lds) {
     __shared__ uint32_t tile[64 * 64];
-    // consecutive workgroups: consecutive padded groups of one column tile
-    // (as in quant_col_kernel)
-    const int64_t pt = gridDim.x / col_tiles;
-    const int64_t p = blockIdx.x % pt;
-    const int64_t c0 = (blockIdx.x / pt) * 64;
-    int e;
-    int64_t j;
-    find_expert_group(offsets, G, p, e, j);
-    if (e < 0) return;  // past the last group (the grid is sized for a bound)
-    const int64_t r0 = (int64_t)offsets[e] + 128 * j;
-    const int64_t left = (int64_t)offsets[e + 1] - r0;
-    const int nrows = left < 128 ? (int)left : 128;
-    col_group_tile<POW2>(x + r0 * ldx, nrows, cols, ldx, c0, q + p * 128, ldq, s + p * lds, tile);
+    __shared__ int64_t wsum[4];
+    const int e = (int)(blockIdx.x % (unsigned)G);
+    const int64_t c0 = (int64_t)(blockIdx.x / (unsigned)G) * 64;
+    const int64_t r0 = offsets[e], r1 = offsets[e + 1];
+    const int64_t ng = (r1 - r0 + 127) / 128;
+    if (ng <= 0) return;  // an expert without tokens has no groups
+    ColLoads L;
+    col_group_load(x + r0 * ldx, (int)(r1 - r0 < 128 ? r1 - r0 : 128), cols, ldx, c0, L);
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int64_t before = 0;
+    for (int i = t; i < e; i += 256) before += ((int64_t)offsets[i + 1] - offsets[i] + 127) / 128;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) before += __shfl_xor(before, d);
+    if (lane == 0) wsum[wave] = before;
+    __syncthreads();
+    const int64_t first = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+
+    for (int64_t j = 0; j < ng; j++) {
+        if (j > 0) {
+            __syncthreads();  // the previous group's tile has been read
+            const int64_t rj = r0 + 128 * j;
+            col_group_load(x + rj * ldx, (int)(r1 - rj < 128 ? r1 - rj : 128), cols, ldx, c0, L);
+        }
+        col_group_finish<POW2>(L, cols, c0, q + (first + j) * 128, ldq, s + (first + j) * lds, tile);
+    }
 }
 
 // ---- 128x128 blocks ----------------------------------------------------------------------
@@ -564,14 +568,14 @@ hipError_t launch_quant_grouped_col(const uint16_t* x, int64_t T, int64_t cols, 
                                     const int32_t* offsets, bool pow2, uint8_t* q, int64_t ldq, float* s,
                                     int64_t lds, hipStream_t st) {
     if (cols == 0 || G == 0) return hipSuccess;
-    const int64_t ct = (cols + 63) / 64, groups = (T + 127) / 128 + G;
-    const dim3 grid((unsigned)(ct * groups));
+    const int64_t ct = (cols + 63) / 64;
+    const dim3 grid((unsigned)(ct * G));
     if (pow2)
         hipLaunchKernelGGL(quant_grouped_col_kernel<true>, grid, dim3(256), 0, st, x, cols, ldx, G, offsets, q, ldq,
-                           s, lds, ct);
+                           s, lds);
     else
         hipLaunchKernelGGL(quant_grouped_col_kernel<false>, grid, dim3(256), 0, st, x, cols, ldx, G, offsets, q, ldq,
-                           s, lds, ct);
+                           s, lds);
     return hipGetLastError();
 }
 
