@@ -140,6 +140,20 @@ struct Shape<5> {
     }
 };
 
+//  Shape 7: 256 x 224, waves of 64 x 112 (seven 16-column fragments),
+//    two stages: the per-column-scale (Wgrad) GEMMs whose 256 x 256 tiles
+//    would leave part of the CUs idle for a whole round -- the expert Wgrad
+//    2048 x 7168 is 224 wide tiles on 256 CUs, or 256 of these.  Only the
+//    tile kind (a 112-column wave slot may straddle a 128-column weight
+//    block) and the FP32-scale FP8 mode.
+template <>
+struct Shape<7> {
+    static constexpr int BM = 256, BN = 224;
+    static constexpr int WM = 64, WN = 112;
+    static constexpr int STAGES = 2;
+    __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<0>::wave_grid(wave, wm, wn); }
+};
+
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
 template <int SH>
@@ -149,7 +163,8 @@ struct Lds {
     static constexpr int B = BM * 128;
     static constexpr int SA = B + BN * 128;
     static constexpr int SB = SA + BM * 4;
-    static constexpr int STAGE = SB + BN * 4;
+    // the per-column scales are staged 64 at a time
+    static constexpr int STAGE = SB + (BN + 63) / 64 * 64 * 4;
     static constexpr int BYTES = STAGE * Shape<SH>::STAGES;
 };
 
@@ -247,7 +262,7 @@ template <int SH, int KIND>
 struct Stager {
     static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     static constexpr int NA = BM / 8 / LOADERS, NB = BN / 8 / LOADERS;
-    static constexpr int SA_INS = BM / 64, SB_INS = KIND == 1 ? BN / 64 : 1;
+    static constexpr int SA_INS = BM / 64, SB_INS = KIND == 1 ? (BN + 63) / 64 : 1;
     static_assert(SA_INS <= LOADERS && SB_INS <= LOADERS, "one instruction per loader for each scale");
     static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
     uint32_t va[NA], vb[NB], vsa, vsb;
@@ -754,7 +769,7 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
 // loop (wait_and_barrier<0>) before this runs.
 template <int SH>
 struct Epi {
-    static constexpr int W = 128;  // columns per image
+    static constexpr int W = SH == 7 ? 112 : 128;  // columns per image
     static constexpr int LD = W + 4;
     static_assert(Shape<SH>::BM * LD * 4 <= Lds<SH>::BYTES, "the image fits in the stages");
     static_assert(Shape<SH>::BN % W == 0 && W % Shape<SH>::WN == 0, "waves' columns tile the images");
@@ -776,7 +791,9 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
     constexpr int LPR = W / 4;                // lanes per row
     constexpr int RPI = STORE_THREADS / LPR;  // rows per pass
     const int t = (int)threadIdx.x - LOADERS * 64;
-    if (t < 0) return;  // the loader waves do not store
+    // the loader waves do not store (nor, with 112-column images, the
+    // threads past a whole number of rows)
+    if (t < 0 || t >= RPI * LPR) return;
     const int col = (t % LPR) * 4;
     const int64_t n = n0 + col;
     if constexpr (OUT <= 1) {
@@ -1249,7 +1266,7 @@ static int device_cus() {
 // workgroups, counting a round of the narrow tiles as 0.65 of a round of
 // the wide ones (their measured time per tile): 4096 x 18432, 4.5 rounds
 // of wide tiles, becomes 4 rounds of wide tiles and one of narrow ones.
-int64_t wide_columns(int64_t M, int64_t N, int cus) {
+int64_t wide_columns(int64_t M, int64_t N, int cus, double* cost_out) {
     const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
     int64_t best_n1 = 256 * tn;  // every column on wide tiles
     double best = (double)((tm * tn + cus - 1) / cus);
@@ -1261,7 +1278,15 @@ int64_t wide_columns(int64_t M, int64_t N, int cus) {
             best_n1 = 256 * n1t;
         }
     }
+    if (cost_out) *cost_out = best;
     return best_n1;
+}
+
+// Rounds of 256 x 224 tiles, in the wide tile's rounds (a 256 x 224 tile is
+// 7/8 of a wide tile's work).
+static double cols224_cost(int64_t M, int64_t N, int cus) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 223) / 224);
+    return 0.875 * (double)((tiles + cus - 1) / cus);
 }
 
 // Split-K and the f16 path use shape 0; the FP8 paths gemm_wide_kernel,
@@ -1271,7 +1296,17 @@ static void launch_dense(const GemmArgs& g, hipStream_t st) {
     if constexpr (ACC == 0 || SPLIT) {
         launch_shape<ACC, 0, KIND, OUT, SPLIT>(g, st);
     } else {
-        const int64_t n1 = wide_columns(g.M, g.N, device_cus());
+        const int cus = device_cus();
+        double wide_cost = 0.0;
+        const int64_t n1 = wide_columns(g.M, g.N, cus, &wide_cost);
+        if constexpr (ACC == 1 && KIND == 1 && OUT <= 1) {
+            // per-column scales, FP32-scale mode: 256 x 224 tiles where
+            // their rounds come out fuller (2048 x 7168: one full round)
+            if (cols224_cost(g.M, g.N, cus) < wide_cost - 0.05) {
+                launch_shape<1, 7, 1, OUT, false>(g, st);
+                return;
+            }
+        }
         const int64_t tiles_m = (g.M + Shape<1>::BM - 1) / Shape<1>::BM;
         const int64_t narrow_n = n1 < g.N ? (g.N - n1 + Shape<0>::BN - 1) / Shape<0>::BN : 0;
         const int64_t wgs = tiles_m * (n1 / Shape<1>::BN) + tiles_m * narrow_n;

@@ -75,8 +75,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K);
 // Workspace bytes the dense GEMM needs for this shape.
 size_t gemm_workspace(int64_t M, int64_t N, int64_t K);
 // Output columns the FP8 dense paths run on 256 x 256 tiles (the rest on
-// 256 x 128 tiles), given the device's compute units.
-int64_t wide_columns(int64_t M, int64_t N, int cus);
+// 256 x 128 tiles), given the device's compute units; *cost_out, if given,
+// receives the split's cost in rounds of 256 x 256 tiles.
+int64_t wide_columns(int64_t M, int64_t N, int cus, double* cost_out = nullptr);
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);

@@ -272,6 +272,23 @@ def _dense_fprop_reference(mode):
     return wqx, wsx, wqw, wsw, r, rabs
 
 
+@pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
+def test_wgrad_224_column_tiles(hip, orc, out):
+    """Per-column-scale GEMMs (Wgrad) in the FP32-scale FP8 mode on shapes
+    where 256 x 224 tiles fill the CUs better than 256 x 256 ones (on a
+    256-CU MI355X): dW[1000x2016] over 384 tokens (nine whole 224-column
+    tiles, ragged rows) and dW[520x2000] over 256 tokens (a last tile of 208
+    columns, a last row tile of 8 rows); every output compared."""
+    for i, (T, Nw, C) in enumerate([(384, 1000, 2016), (256, 520, 2000)]):
+        dY = inputs.random_bf16(161 + 2 * i, (T, Nw), sd=1e-3)
+        X = inputs.random_bf16(162 + 2 * i, (T, C))
+        qdt, sdt, _, wqdt, wsdt, _ = quant_both(hip, orc, dY, "col", 0)
+        qxt, sxt, _, wqxt, wsxt, _ = quant_both(hip, orc, X, "col", 0)
+        dw = hip.linear_wgrad(qdt, sdt, qxt, sxt, out, accum=1)
+        r, rabs = full(orc, wqdt, wsdt, wqxt, wsxt, 1, wsxt.shape[1], 0)
+        check(out_f64(dw), r, rabs, out, 1, T // 128, f"wgrad 224-column tiles {Nw}x{C}x{T} out={out}")
+
+
 @pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
 def test_group_counts_mixed_tiles(hip, orc, accum):
     """K = 128 .. 896 (one to seven K groups: the single-group path, odd
