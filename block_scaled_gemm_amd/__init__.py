@@ -89,6 +89,8 @@ def lib():
         L.fp8_grouped_gemm_kgrouped.restype = i32
         L.fp8_grouped_gemm_kgrouped.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                                 i64, i64, i32, i32, vp]
+        L.fp8_scales_are_pow2.restype = i32
+        L.fp8_scales_are_pow2.argtypes = [vp, i64, i64, i64, i64, vp, vp]
         L.fp8_gemm_blockscaled_quant.restype = i32
         L.fp8_gemm_blockscaled_quant.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i32, i64, i64, i32,
                                                  vp, i64, vp, i64, i32, vp]
@@ -236,6 +238,37 @@ def gemm_workspace_bytes(M, N, K):
     return int(lib().fp8_gemm_workspace_bytes(M, N, K))
 
 
+def scales_are_pow2(s, rows=None, cols=None, ld_r=None, ld_c=None):
+    """Whether every scale of s is a positive normal power of two (entry
+    (r, c) at s[r*ld_r + c*ld_c]; by default the 2-D tensor s itself).
+    Synchronises the stream to read the answer.  Any strides (a view of a
+    larger array is checked on its own entries)."""
+    if not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype != torch.float32:
+        raise TypeError("s must be a float32 CUDA (HIP) tensor")
+    if rows is None:
+        rows, cols = s.shape
+        ld_r, ld_c = s.stride(0), s.stride(1)
+    flag = torch.empty(1, dtype=torch.int32, device=s.device)
+    _check(lib().fp8_scales_are_pow2(_ptr(s), int(rows), int(cols), int(ld_r), int(ld_c), _ptr(flag), _stream()),
+           "fp8_scales_are_pow2")
+    return bool(flag.item())
+
+
+def _check_pow2_mode(accum, sa, a_rows, sb, bscale_kind, sb_s0, sb_s1, n, groups):
+    """With FP8BS_CHECK_POW2 set in the environment, refuse the power-of-two
+    MFMA mode on scales that are not powers of two (a debugging aid: it
+    synchronises the stream)."""
+    if accum != ACCUM_MFMA8_POW2 or not os.environ.get("FP8BS_CHECK_POW2"):
+        return
+    ok = scales_are_pow2(sa, groups, a_rows, _ld(sa), 1)
+    if bscale_kind == BSCALE_BLOCK:
+        ok = ok and scales_are_pow2(sb, (n + 127) // 128, groups, sb_s0, sb_s1)
+    else:
+        ok = ok and scales_are_pow2(sb, groups, n, sb_s0, 1)
+    if not ok:
+        raise ValueError("ACCUM_MFMA8_POW2 with scales that are not powers of two")
+
+
 def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_BF16, d=None,
                          workspace=None, accum=ACCUM_FP32):
     """D[m,n] = sum_g sa[g,m] * SB(n,g) * sum_{k in g} dec(a[m,k]) dec(b[n,k]).
@@ -249,6 +282,7 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind, sb_s0, sb_s1, out_dtype=OUT_
     N = b.shape[0]
     if b.shape[1] != K:
         raise ValueError("a and b disagree on K")
+    _check_pow2_mode(accum, sa, M, sb, bscale_kind, sb_s0, sb_s1, N, K // 128)
     dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
     if d is None:
         d = torch.empty((M, N), dtype=dt, device=a.device)
@@ -322,6 +356,11 @@ def fp8_grouped_gemm(offsets, a, sa, b, sb, out_dtype=OUT_BF16, rows_bound=None,
     if not b.is_contiguous() or not sb.is_contiguous():
         raise ValueError("b and sb must be contiguous [G, N, K] / [G, N/128, K/128]")
     rows = a.shape[0] if rows_bound is None else int(rows_bound)
+    if accum == ACCUM_MFMA8_POW2 and os.environ.get("FP8BS_CHECK_POW2"):
+        # every expert's block scales as one [G*N/128, K/128] array
+        if not (scales_are_pow2(sa, K // 128, rows, _ld(sa), 1) and
+                scales_are_pow2(sb, G * ((N + 127) // 128), K // 128, K // 128, 1)):
+            raise ValueError("ACCUM_MFMA8_POW2 with scales that are not powers of two")
     dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
     if d is None:
         d = torch.empty((rows, N), dtype=dt, device=a.device)

@@ -160,6 +160,15 @@ FP8BS_EXPORT int fp8_requant_col(const uint8_t* q, int64_t rows, int64_t cols, i
                                                 ldqt, st, ldst, (hipStream_t)stream));
 }
 
+FP8BS_EXPORT int fp8_scales_are_pow2(const float* s, int64_t rows, int64_t cols, int64_t ld_r, int64_t ld_c,
+                                     int32_t* flag, void* stream) {
+    if (rows < 0 || cols < 0 || ld_r < 0 || ld_c < 0 || !flag) return FP8BS_ERR_ARG;
+    if (rows > 0 && cols > 0 && !s) return FP8BS_ERR_ARG;
+    if (!aligned(s, 4) || !aligned(flag, 4)) return FP8BS_ERR_ALIGN;
+    if (int r = check_device()) return r;
+    return hip_status(fp8bs::launch_scales_pow2_check(s, rows, cols, ld_r, ld_c, flag, (hipStream_t)stream));
+}
+
 FP8BS_EXPORT size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
     return fp8bs::gemm_workspace(M, N, K);

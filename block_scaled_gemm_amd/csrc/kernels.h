@@ -29,6 +29,8 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
                              int64_t ldqr, float* sr, int64_t ldsr, uint8_t* qc, int64_t ldqc, float* sc,
                              int64_t ldsc, hipStream_t st);
 
+hipError_t launch_scales_pow2_check(const float* s, int64_t rows, int64_t cols, int64_t ld_r, int64_t ld_c,
+                                    int32_t* flag, hipStream_t st);
 hipError_t launch_requant_col(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
                               int64_t lds, bool pow2, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
                               hipStream_t st_);

@@ -48,6 +48,37 @@ hipError_t launch_cast(const float* x, int64_t n, uint8_t* q, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ---- power-of-two scale check ---------------------------------------------------------
+//
+// Writes 1 to *flag, then any thread that meets an entry which is not a
+// positive normal power of two (sign 0, exponent field 1..254, mantissa 0)
+// writes 0: every writer stores the same value.
+
+__global__ void pow2_flag_init_kernel(int32_t* __restrict__ flag) { *flag = 1; }
+
+__global__ __launch_bounds__(256) void pow2_check_kernel(const float* __restrict__ s, int64_t rows, int64_t cols,
+                                                         int64_t ld_r, int64_t ld_c, int32_t* __restrict__ flag) {
+    const int64_t n = rows * cols;
+    bool ok = true;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / cols, c = i % cols;
+        const uint32_t b = __float_as_uint(s[r * ld_r + c * ld_c]);
+        const uint32_t e = (b >> 23) & 0xFFu;
+        ok = ok && (b & 0x807FFFFFu) == 0 && e != 0 && e != 0xFF;
+    }
+    if (!ok) *flag = 0;
+}
+
+hipError_t launch_scales_pow2_check(const float* s, int64_t rows, int64_t cols, int64_t ld_r, int64_t ld_c,
+                                    int32_t* flag, hipStream_t st) {
+    hipLaunchKernelGGL(pow2_flag_init_kernel, dim3(1), dim3(1), 0, st, flag);
+    const int64_t n = rows * cols;
+    if (n == 0) return hipGetLastError();
+    const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(pow2_check_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, rows, cols, ld_r, ld_c, flag);
+    return hipGetLastError();
+}
+
 // ---- 1x128 groups along rows ---------------------------------------------------------
 //
 // A workgroup covers 4*RPW rows x 512 columns: each wave takes RPW rows,

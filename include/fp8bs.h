@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 4
+#define FP8BS_ABI_VERSION 5
 
 /* Largest lda / ldb (bytes) the GEMMs take: the kernels address the rows of
  * a 256-row tile with 32-bit offsets (255 * 2^24 + 127 < 2^32). */
@@ -104,7 +104,8 @@ enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_F32 = 1 };
  *    accumulator, with no promotion step -- the block-scaled
  *    microscaling form of the method ([cameseeing-1171527], passage relating
  *    the fine-grained scaling to microscaling formats).  Scales that are not
- *    powers of two give wrong results; the error contract is that of
+ *    powers of two give wrong results without an error
+ *    (fp8_scales_are_pow2 checks them); the error contract is that of
  *    FP8BS_ACCUM_MFMA8. */
 enum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_MFMA8 = 1, FP8BS_ACCUM_MFMA8_POW2 = 2 };
 
@@ -267,6 +268,32 @@ int fp8_quant_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
 int fp8_requant_col(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
                     const float *s, int64_t lds, int scale_mode, uint8_t *qt,
                     int64_t ldqt, float *st, int64_t ldst, void *stream);
+
+/*
+ * fp8_scales_are_pow2 -- whether every scale of a power-of-two
+ * quantisation really is one.  FP8BS_ACCUM_MFMA8_POW2 hands the scales to
+ * the matrix cores as E8M0 exponents ([cameseeing-1171527], passage
+ * relating the fine-grained scaling to microscaling formats), which keep
+ * only the exponent: any other scale gives wrong products without an
+ * error.  This check lets a caller (or a debug build of its own) verify
+ * the scales first.
+ *
+ *   s      fp32 array, entry (r, c) at s[r*ld_r + c*ld_c], r < rows, c < cols
+ *          (ld_r, ld_c >= 0; e.g. fp8_quant_tile's row scales: rows = K/128,
+ *          cols = M, ld_r = lds, ld_c = 1; block scales addressed as the
+ *          GEMM's SB: rows = ceil(N/128), cols = K/128, ld_r = sb_s0,
+ *          ld_c = sb_s1).
+ *   flag   one int32 in device memory, written on the stream: 1 when every
+ *          entry is a positive normal power of two (sign 0, exponent field
+ *          1..254, mantissa 0), else 0; an empty array gives 1.  The caller
+ *          reads it after synchronising the stream.
+ * Alignment: s and flag 4-byte aligned.
+ * Errors: ERR_ARG (negative size or stride, null pointer), ERR_ALIGN,
+ * ERR_DEVICE, ERR_HIP.
+ */
+int fp8_scales_are_pow2(const float *s, int64_t rows, int64_t cols,
+                        int64_t ld_r, int64_t ld_c, int32_t *flag,
+                        void *stream);
 
 /*
  * fp8_gemm_blockscaled -- block-scaled FP8 GEMM with FP32 promotion every

@@ -26,7 +26,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["fp8_quant_tile", "fp8_quant_block", "fp8_quant_dual", "fp8_requant_col", "fp8_gemm_blockscaled",
               "fp8_grouped_gemm_strided", "fp8_quant_tile_grouped_col", "fp8_grouped_gemm_kgrouped",
-              "fp8_gemm_blockscaled_quant", "fp8_gemm_blockscaled_noalloc",
+              "fp8_gemm_blockscaled_quant", "fp8_gemm_blockscaled_noalloc", "fp8_scales_are_pow2",
               "fp8_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_cast_e4m3",
               "fp8bs_abi_version", "fp8bs_status_string"]:
         assert n in names
@@ -46,7 +46,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bs.abi_version() == 4
+    assert bs.abi_version() == 5
     for s in range(7):
         assert bs.status_string(s)
     assert "unknown" in bs.status_string(99)
@@ -302,3 +302,14 @@ def test_no_device_is_reported():
         pytest.skip("a GPU is present: this check is for GPU-less hosts")
     assert _tile() == DEVICE
     assert _gemm() == DEVICE
+
+
+def test_pow2_check_validation():
+    L = bs.lib()
+    chk = lambda *a: L.fp8_scales_are_pow2(*a, None)
+    assert chk(FAKE, -1, 4, 4, 1, FAKE) == ARG          # negative size
+    assert chk(FAKE, 4, 4, -4, 1, FAKE) == ARG          # negative stride
+    assert chk(FAKE, 4, 4, 4, 1, None) == ARG           # no flag
+    assert chk(None, 4, 4, 4, 1, FAKE) == ARG           # no scales
+    assert chk(FAKE + 2, 4, 4, 4, 1, FAKE) == ALIGN     # misaligned scales
+    assert chk(FAKE, 4, 4, 4, 1, FAKE + 1) == ALIGN     # misaligned flag
