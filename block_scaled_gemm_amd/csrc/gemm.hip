@@ -154,6 +154,17 @@ struct Shape<7> {
     __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<0>::wave_grid(wave, wm, wn); }
 };
 
+//  Shape 8: shape 5's tile and waves with 64-column output images: the
+//    K-grouped Wgrad that keeps B resident passes its images through its
+//    34 KB A ring.
+template <>
+struct Shape<8> {
+    static constexpr int BM = 128, BN = 128;
+    static constexpr int WM = 32, WN = 64;
+    static constexpr int STAGES = 2;
+    __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<5>::wave_grid(wave, wm, wn); }
+};
+
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
 template <int SH>
@@ -485,6 +496,21 @@ __device__ __forceinline__ void compute_f32_block(const uint8_t* stage, int wm, 
     cp[1] = cn[1];
 }
 
+// LDS addresses of one K group's operands (within one stage, or in
+// separate regions where a kernel keeps an operand resident).
+struct StagePtrs {
+    const uint8_t* a;  // A codes [BM][128], rows swizzled as f8_off
+    const uint8_t* b;  // B codes [BN][128]
+    const float* sa;   // A row scales [BM]
+    const float* sb;   // B scales: per column [BN] (tile kind) or the block scalars
+};
+
+template <int SH>
+__device__ __forceinline__ StagePtrs stage_ptrs(const uint8_t* stage) {
+    return StagePtrs{stage + Lds<SH>::A, stage + Lds<SH>::B, (const float*)(stage + Lds<SH>::SA),
+                     (const float*)(stage + Lds<SH>::SB)};
+}
+
 // ==== ACC_MFMA8 path: FP8 matrix cores, one MFMA per K group =============================
 //
 // Lane l feeds bytes [32(l/16), 32(l/16)+32) of its row: chunks 2(l/16) and
@@ -528,13 +554,13 @@ __device__ __forceinline__ void offset_second_wave() {
 // wave's shorter side stay in registers while those of the longer side
 // stream past them.  A wave's WN <= 128 columns lie in one 128-column block.
 template <int SH, int KIND>
-__device__ __forceinline__ void compute_mfma8(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
+__device__ __forceinline__ void compute_mfma8(const StagePtrs& sp, int wm, int wn, int lane, int m_valid,
                                               v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ]) {
     constexpr int MI = Sub<SH>::MI, NJ = Sub<SH>::NJ;
-    const uint8_t* la = stage + Lds<SH>::A;
-    const uint8_t* lb = stage + Lds<SH>::B;
-    const float* lsa = (const float*)(stage + Lds<SH>::SA);
-    const float* lsb = (const float*)(stage + Lds<SH>::SB);
+    const uint8_t* la = sp.a;
+    const uint8_t* lb = sp.b;
+    const float* lsa = sp.sa;
+    const float* lsb = sp.sb;
     const int mbase = wm * Shape<SH>::WM, nbase = wn * Shape<SH>::WN;
     const int c0 = 2 * (lane >> 4);
     if (mbase >= m_valid) return;
@@ -627,13 +653,13 @@ __device__ __forceinline__ void compute_mfma8(const uint8_t* stage, int wm, int 
 __device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
 
 template <int SH, int KIND>
-__device__ __forceinline__ void compute_mfma8_pow2(const uint8_t* stage, int wm, int wn, int lane, int m_valid,
+__device__ __forceinline__ void compute_mfma8_pow2(const StagePtrs& sp, int wm, int wn, int lane, int m_valid,
                                                    v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ]) {
     constexpr int MI = Sub<SH>::MI, NJ = Sub<SH>::NJ;
-    const uint8_t* la = stage + Lds<SH>::A;
-    const uint8_t* lb = stage + Lds<SH>::B;
-    const float* lsa = (const float*)(stage + Lds<SH>::SA);
-    const float* lsb = (const float*)(stage + Lds<SH>::SB);
+    const uint8_t* la = sp.a;
+    const uint8_t* lb = sp.b;
+    const float* lsa = sp.sa;
+    const float* lsb = sp.sb;
     const int mbase = wm * Shape<SH>::WM, nbase = wn * Shape<SH>::WN;
     const int c0 = 2 * (lane >> 4);
     if (mbase >= m_valid) return;
@@ -769,7 +795,7 @@ __device__ __forceinline__ void store4(void* d, int64_t ldd, int64_t m, int64_t 
 // loop (wait_and_barrier<0>) before this runs.
 template <int SH>
 struct Epi {
-    static constexpr int W = SH == 7 ? 112 : 128;  // columns per image
+    static constexpr int W = SH == 7 ? 112 : SH == 8 ? 64 : 128;  // columns per image
     static constexpr int LD = W + 4;
     static_assert(Shape<SH>::BM * LD * 4 <= Lds<SH>::BYTES, "the image fits in the stages");
     static_assert(Shape<SH>::BN % W == 0 && W % Shape<SH>::WN == 0, "waves' columns tile the images");
@@ -953,9 +979,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
             compute_f32_tile<SH>(stage, wm, wn, lane, m_valid, acc);
         } else {
             if constexpr (ACC == 1)
-                compute_mfma8<SH, KIND>(stage, wm, wn, lane, m_valid, acc);
+                compute_mfma8<SH, KIND>(stage_ptrs<SH>(stage), wm, wn, lane, m_valid, acc);
             else
-                compute_mfma8_pow2<SH, KIND>(stage, wm, wn, lane, m_valid, acc);
+                compute_mfma8_pow2<SH, KIND>(stage_ptrs<SH>(stage), wm, wn, lane, m_valid, acc);
         }
     };
     for (int64_t g = g0; g < g1; g += S) {
@@ -1195,6 +1221,106 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
 }
 
+// K-grouped Wgrad, experts of at most two K groups: the workgroup's B tile
+// (its column tile of every group of the expert) is staged once and stays
+// in LDS while the strip's row tiles stage only their A groups; a tile's
+// fp32 output goes out through the A ring in two 64-column images.  Other
+// experts take the kgrouped2 path.  LDS: B groups [2][codes 16 KB + 128
+// column scales], then the A ring [2][codes 16 KB + 128 row scales, padded
+// so that the ring holds a 128 x 64 fp32 image].
+constexpr int KG3_BGROUP = 128 * 128 + 128 * 4;
+constexpr int KG3_ASTAGE = 128 * 128 + 128 * 4 + 512;
+constexpr int KG3_A = 2 * KG3_BGROUP;
+constexpr int KG3_BYTES = KG3_A + 2 * KG3_ASTAGE;
+static_assert(128 * Epi<8>::LD * 4 <= 2 * KG3_ASTAGE && Lds<5>::BYTES <= KG3_BYTES, "the K-grouped LDS map");
+
+__device__ __forceinline__ void kg3_issue_a(const Stager<5, 1>& stg, const Tile& T, int64_t g, uint8_t* dst,
+                                            int wave) {
+    const uint8_t* a = T.a + T.m0 * T.lda + g * 128;
+    const uint32_t base = lds_addr(dst);
+#pragma unroll
+    for (int ins = 0; ins < Stager<5, 1>::NA; ins++) dma16s(stg.va[ins], a, base + (ins * LOADERS + wave) * 8 * 128);
+    if (wave < Stager<5, 1>::SA_INS) dma4s(stg.vsa, T.sa + g * T.ldsa + T.m0, base + 128 * 128 + wave * 256);
+}
+
+__device__ __forceinline__ void kg3_issue_b(const Stager<5, 1>& stg, const Tile& T, int64_t g, uint8_t* dst,
+                                            int wave) {
+    const uint8_t* b = T.b + T.n0 * T.ldb + g * 128;
+    const uint32_t base = lds_addr(dst);
+#pragma unroll
+    for (int ins = 0; ins < Stager<5, 1>::NB; ins++) dma16s(stg.vb[ins], b, base + (ins * LOADERS + wave) * 8 * 128);
+    if (wave < Stager<5, 1>::SB_INS) dma4s(stg.vsb, T.sb + g * T.sb_s0 + T.n0, base + 128 * 128 + wave * 256);
+}
+
+template <int ACC, int OUT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void kgrouped3_kernel(
+    GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[KG3_BYTES];
+    const int64_t strips = (tiles_m + KSTRIP - 1) / KSTRIP;
+    const int64_t per = tiles_n * strips;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t e = wid / per;
+    const int64_t tn = (wid % per) % tiles_n, strip = (wid % per) / tiles_n;
+    const int64_t g0 = expert_first_group(p.offsets, e);
+    const int64_t ng = ((int64_t)p.offsets[e + 1] - p.offsets[e] + 127) / 128;
+
+    Tile T;
+    T.n0 = tn * 128;
+    T.m_end = p.M;
+    T.n_end = p.N;
+    T.a = p.a;
+    T.lda = p.lda;
+    T.sa = p.sa;
+    T.ldsa = p.ldsa;
+    T.b = p.b;
+    T.ldb = p.ldb;
+    T.sb = p.sb;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = 0;
+    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT ? 4 : 2);
+    const int64_t tm0 = strip * KSTRIP, tm1 = tm0 + KSTRIP < tiles_m ? tm0 + KSTRIP : tiles_m;
+    if (ng == 0 || ng > 2) {
+        for (int64_t tm = tm0; tm < tm1; tm++) {
+            T.m0 = tm * 128;
+            run_tile<ACC, 5, 1, OUT>(T, g0, g0 + ng, d, p.ldd, smem);
+        }
+        return;
+    }
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    int wm, wn;
+    Shape<8>::wave_grid(wave, wm, wn);
+    Stager<5, 1> stg;
+    T.m0 = tm0 * 128;
+    stg.init(T, wave, lane);
+    if (wave < LOADERS)
+        for (int k = 0; k < ng; k++) kg3_issue_b(stg, T, g0 + k, smem + k * KG3_BGROUP, wave);
+    for (int64_t tm = tm0; tm < tm1; tm++) {
+        T.m0 = tm * 128;
+        if (tm != tm0) stg.init(T, wave, lane);
+        if (wave < LOADERS)
+            for (int k = 0; k < ng; k++) kg3_issue_a(stg, T, g0 + k, smem + KG3_A + k * KG3_ASTAGE, wave);
+        wait_and_barrier<0>(wave);  // this tile's A groups (and, the first time, B) have landed
+        const int m_valid = (int)(T.m_end - T.m0 < 128 ? T.m_end - T.m0 : 128);
+        v4f acc[Sub<8>::MI][Sub<8>::NJ];
+#pragma unroll
+        for (int i = 0; i < Sub<8>::MI; i++)
+#pragma unroll
+            for (int j = 0; j < Sub<8>::NJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < ng; k++) {
+            const uint8_t* as = smem + KG3_A + k * KG3_ASTAGE;
+            const uint8_t* bg = smem + k * KG3_BGROUP;
+            const StagePtrs sp{as, bg, (const float*)(as + 128 * 128), (const float*)(bg + 128 * 128)};
+            if constexpr (ACC == 1)
+                compute_mfma8<8, 1>(sp, wm, wn, lane, m_valid, acc);
+            else
+                compute_mfma8_pow2<8, 1>(sp, wm, wn, lane, m_valid, acc);
+        }
+        __syncthreads();  // every wave is done with the A ring, which the images reuse
+        store_mfma8<8, OUT>(acc, T, wm, wn, lane, d, p.ldd, smem + KG3_A);
+    }
+}
+
 // Sum split-K partials in split order and convert.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
@@ -1391,9 +1517,9 @@ static hipError_t launch_kgrouped_acc(const GemmArgs& g, hipStream_t st) {
         const int64_t tiles_m = (g.M + 127) / 128, tiles_n = (g.N + 127) / 128;
         const dim3 grid((unsigned)(tiles_n * ((tiles_m + KSTRIP - 1) / KSTRIP) * g.G));
         if (g.out_f32)
-            hipLaunchKernelGGL((kgrouped2_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+            hipLaunchKernelGGL((kgrouped3_kernel<ACC, 1>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
         else
-            hipLaunchKernelGGL((kgrouped2_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
+            hipLaunchKernelGGL((kgrouped3_kernel<ACC, 0>), grid, dim3(THREADS), 0, st, g, tiles_m, tiles_n);
         return hipGetLastError();
     }
     const int64_t tiles_m = (g.M + Shape<0>::BM - 1) / Shape<0>::BM;
