@@ -1183,44 +1183,6 @@ __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t t
     }
 }
 
-// The FP8 modes' K-grouped Wgrad on shape 5, two workgroups per CU
-// (128 VGPRs per lane); work split as kgrouped_kernel.
-template <int ACC, int OUT>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void kgrouped2_kernel(
-    GemmArgs p, int64_t tiles_m, int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<5>::BYTES];
-    // workgroup = (expert, strip of KSTRIP m-tiles, n-tile); consecutive
-    // workgroups take consecutive n-tiles of the same rows, so the tiles in
-    // flight together write adjacent 512 B pieces of the same output rows
-    const int64_t strips = (tiles_m + KSTRIP - 1) / KSTRIP;
-    const int64_t per = tiles_n * strips;
-    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t e = wid / per;
-    const int64_t tn = (wid % per) % tiles_n, strip = (wid % per) / tiles_n;
-    const int64_t g0 = expert_first_group(p.offsets, e);
-    const int64_t g1 = g0 + ((int64_t)p.offsets[e + 1] - p.offsets[e] + 127) / 128;
-
-    Tile T;
-    T.n0 = tn * Shape<5>::BN;
-    T.m_end = p.M;
-    T.n_end = p.N;
-    T.a = p.a;
-    T.lda = p.lda;
-    T.sa = p.sa;
-    T.ldsa = p.ldsa;
-    T.b = p.b;
-    T.ldb = p.ldb;
-    T.sb = p.sb;
-    T.sb_s0 = p.sb_s0;
-    T.sb_s1 = 0;
-    void* d = (uint8_t*)p.d + e * p.d_estride * (OUT ? 4 : 2);
-    const int64_t tm_end = (strip + 1) * KSTRIP < tiles_m ? (strip + 1) * KSTRIP : tiles_m;
-    for (int64_t tm = strip * KSTRIP; tm < tm_end; tm++) {
-        T.m0 = tm * Shape<5>::BM;
-        run_tile<ACC, 5, 1, OUT>(T, g0, g1, d, p.ldd, smem);
-    }
-}
-
 // K-grouped Wgrad, experts of at most two K groups: the workgroup's B tile
 // (its column tile of every group of the expert) is staged once and stays
 // in LDS while the strip's row tiles stage only their A groups; a tile's
