@@ -123,11 +123,11 @@ struct Shape<2> {
     }
 };
 
-//  Shape 5: shape 2's 128 x 128 tile and wave grid with two stages
-//    (66 KB, which the 128 x 128 fp32 output image also fits): the
-//    K-grouped Wgrad, whose experts hold one or two K groups and whose
-//    cost is the fp32 output, runs two workgroups per CU with it, so one
-//    workgroup's stores overlap the other's loads and MFMAs.
+//  Shape 5: 128 x 128 with waves of 32 x 64 and two stages (66 KB, which
+//    the 128 x 128 fp32 output image also fits): the K-grouped Wgrad, whose
+//    experts hold one or two K groups and whose cost is the fp32 output,
+//    runs two workgroups per CU with it, so one workgroup's stores overlap
+//    the other's loads and MFMAs.
 template <>
 struct Shape<5> {
     static constexpr int BM = 128, BN = 128;
@@ -1187,7 +1187,8 @@ __global__ __launch_bounds__(THREADS) void kgrouped_kernel(GemmArgs p, int64_t t
 // (its column tile of every group of the expert) is staged once and stays
 // in LDS while the strip's row tiles stage only their A groups; a tile's
 // fp32 output goes out through the A ring in two 64-column images.  Other
-// experts take the kgrouped2 path.  LDS: B groups [2][codes 16 KB + 128
+// experts run each tile through the two-stage pipeline of shape 5.  LDS:
+// B groups [2][codes 16 KB + 128
 // column scales], then the A ring [2][codes 16 KB + 128 row scales, padded
 // so that the ring holds a 128 x 64 fp32 image].
 constexpr int KG3_BGROUP = 128 * 128 + 128 * 4;
