@@ -810,15 +810,18 @@ __device__ __forceinline__ void put4(float* ep, int row, int col, float v0, floa
 // along n with FP32 / power-of-two scales (the image's 128 columns, starting
 // at output column n0, are one group of every row), codes to d, scales to
 // T.qs.
-template <int SH, int OUT>
+// ALL: every wave stores (kernels that run one tile per workgroup); else
+// the loader waves do not, so that their vmcnt waits for a following
+// tile's groups never count this tile's stores.
+template <int SH, int OUT, bool ALL = false>
 __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T, int64_t n0, void* d,
                                                  int64_t ldd) {
     constexpr int BM = Shape<SH>::BM, W = Epi<SH>::W;
-    constexpr int LPR = W / 4;                // lanes per row
-    constexpr int RPI = STORE_THREADS / LPR;  // rows per pass
-    const int t = (int)threadIdx.x - LOADERS * 64;
-    // the loader waves do not store (nor, with 112-column images, the
-    // threads past a whole number of rows)
+    constexpr int LPR = W / 4;                                  // lanes per row
+    constexpr int RPI = (ALL ? THREADS : STORE_THREADS) / LPR;  // rows per pass
+    const int t = (int)threadIdx.x - (ALL ? 0 : LOADERS * 64);
+    // (with 112-column images, the threads past a whole number of rows
+    // stay idle too)
     if (t < 0 || t >= RPI * LPR) return;
     const int col = (t % LPR) * 4;
     const int64_t n = n0 + col;
@@ -865,7 +868,7 @@ __device__ __forceinline__ void write_tile_image(const float* ep, const Tile& T,
     }
 }
 
-template <int SH, int OUT>
+template <int SH, int OUT, bool ALL = false>
 __device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T, int wm, int wn, int lane,
                                           void* d, int64_t ldd, uint8_t* smem) {
     float* ep = (float*)smem;
@@ -879,11 +882,11 @@ __device__ __forceinline__ void store_f32(const v16f (&acc)[2][2], const Tile& T
                          acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     static_assert(Shape<SH>::BN == Epi<SH>::W, "one image");
     __syncthreads();
-    write_tile_image<SH, OUT>(ep, T, T.n0, d, ldd);
+    write_tile_image<SH, OUT, ALL>(ep, T, T.n0, d, ldd);
     __syncthreads();  // the stages may be refilled by a following tile
 }
 
-template <int SH, int OUT>
+template <int SH, int OUT, bool ALL = false>
 __device__ __forceinline__ void store_mfma8(const v4f (&acc)[Sub<SH>::MI][Sub<SH>::NJ], const Tile& T, int wm,
                                             int wn, int lane, void* d, int64_t ldd, uint8_t* smem) {
     constexpr int W = Epi<SH>::W, WM = Shape<SH>::WM, WN = Shape<SH>::WN;
@@ -900,14 +903,16 @@ __device__ __forceinline__ void store_mfma8(const v4f (&acc)[Sub<SH>::MI][Sub<SH
                              acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
         __syncthreads();
-        write_tile_image<SH, OUT>(ep, T, T.n0 + h * W, d, ldd);
+        write_tile_image<SH, OUT, ALL>(ep, T, T.n0 + h * W, d, ldd);
         __syncthreads();
     }
 }
 
 // ==== one tile: pipelined K loop, then the store ==============================================
 
-template <int ACC, int SH, int KIND, int OUT>
+// ALL_STORE: every wave writes the output (a kernel that runs one tile per
+// workgroup; see write_tile_image).
+template <int ACC, int SH, int KIND, int OUT, bool ALL_STORE = false>
 __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, void* d, int64_t ldd,
                                          uint8_t* smem) {
     constexpr int S = Shape<SH>::STAGES;
@@ -1001,9 +1006,9 @@ __device__ __forceinline__ void run_tile(const Tile& T, int64_t g0, int64_t g1, 
     wait_and_barrier<0>(wave);  // the LDS stages may be reused by a following tile
 
     if constexpr (ACC == 0)
-        store_f32<SH, OUT>(acc, T, wm, wn, lane, d, ldd, smem);
+        store_f32<SH, OUT, ALL_STORE>(acc, T, wm, wn, lane, d, ldd, smem);
     else
-        store_mfma8<SH, OUT>(acc, T, wm, wn, lane, d, ldd, smem);
+        store_mfma8<SH, OUT, ALL_STORE>(acc, T, wm, wn, lane, d, ldd, smem);
 }
 
 // ==== kernels ==========================================================================
@@ -1039,9 +1044,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmArgs p, int64_t tiles
         const int64_t per = (groups + p.splits - 1) / p.splits;
         const int64_t g0 = split * per;
         const int64_t g1 = g0 + per < groups ? g0 + per : groups;
-        run_tile<ACC, SH, KIND, 1>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
+        run_tile<ACC, SH, KIND, 1, true>(T, g0, g1, p.ws + split * p.M * p.ws_ld, p.ws_ld, smem);
     } else {
-        run_tile<ACC, SH, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
+        run_tile<ACC, SH, KIND, OUT, true>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
 
@@ -1078,7 +1083,7 @@ __global__ __launch_bounds__(THREADS) void gemm_wide_kernel(GemmArgs p, int64_t 
         T.m0 = tm * Shape<1>::BM;
         T.n0 = tn * Shape<1>::BN;
         T.n_end = n1 < p.N ? n1 : p.N;
-        run_tile<ACC, 1, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
+        run_tile<ACC, 1, KIND, OUT, true>(T, 0, groups, p.d, p.ldd, smem);
     } else {
         // only launched when n1 < N
         const int64_t tiles_n = (p.N - n1 + Shape<0>::BN - 1) / Shape<0>::BN;
@@ -1086,7 +1091,7 @@ __global__ __launch_bounds__(THREADS) void gemm_wide_kernel(GemmArgs p, int64_t 
         T.m0 = tm * Shape<0>::BM;
         T.n0 = n1 + tn * Shape<0>::BN;
         T.n_end = p.N;
-        run_tile<ACC, 0, KIND, OUT>(T, 0, groups, p.d, p.ldd, smem);
+        run_tile<ACC, 0, KIND, OUT, true>(T, 0, groups, p.d, p.ldd, smem);
     }
 }
 
