@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void quant_grouped_col_kernel(const uint16_t* 
 
 // ---- 128x128 blocks ----------------------------------------------------------------------
 //
-// A workgroup quantises one block.  Thread t owns the 8x8 sub-block at rows
+// The 256 threads of a workgroup quantise a block.  Thread t owns the 8x8 sub-block at rows
 // 8(t/16).., columns 8(t%16)..; each load instruction reads 4 full 256 B
 // row segments.  The block amax is a thread max, a wave max, then a max over
 // the 4 waves through LDS.  The optional transposed copy is an in-register
@@ -359,20 +359,29 @@ __device__ __forceinline__ void block_finish(const uint4 (&v)[8], uint32_t* wmax
     }
 }
 
+// A workgroup takes two blocks side by side (the second absent past the last
+// block column), issuing both blocks' loads before quantising the first:
+// its rows are read as 512 B runs.  On W[32x4096x7168] 502 -> 474 us
+// against one block per workgroup; four blocks per workgroup left too few
+// workgroups for W[18432x7168] (70 -> 75 us).
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ w, int64_t rows,
                                                           int64_t ldw, uint8_t* __restrict__ q,
                                                           int64_t ldq, uint8_t* __restrict__ qt,
                                                           int64_t ldqt, float* __restrict__ s,
                                                           int64_t lds, int64_t col_blocks) {
-    __shared__ uint32_t wmax[4];
+    __shared__ uint32_t wmax[8];
     const int t = threadIdx.x;
-    const int64_t bi = blockIdx.x / col_blocks, bj = blockIdx.x % col_blocks;
+    const int64_t pairs = (col_blocks + 1) / 2;
+    const int64_t bi = blockIdx.x / pairs, bj = 2 * (blockIdx.x % pairs);
+    const bool second = bj + 1 < col_blocks;  // workgroup-uniform
     const int64_t r0 = bi * 128 + 8 * (t >> 4);
     const int64_t c0 = bj * 128 + 8 * (t & 15);
-    uint4 v[8];
+    uint4 v[8], v1[8];
     block_load(w, rows, ldw, r0, c0, v);
+    if (second) block_load(w, rows, ldw, r0, c0 + 128, v1);
     block_finish<POW2>(v, wmax, rows, bi, bj, r0, c0, q, ldq, qt, ldqt, s, lds);
+    if (second) block_finish<POW2>(v1, wmax + 4, rows, bi, bj + 1, r0, c0 + 128, q, ldq, qt, ldqt, s, lds);
 }
 
 // ---- both orientations from one read -------------------------------------------------------
@@ -559,7 +568,7 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int
                               int64_t lds, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t cb = cols / 128, rb = (rows + 127) / 128;
-    const dim3 grid((unsigned)(cb * rb));
+    const dim3 grid((unsigned)(((cb + 1) / 2) * rb));
     if (pow2)
         hipLaunchKernelGGL(quant_block_kernel<true>, grid, dim3(256), 0, st, w, rows, ldw, q, ldq, qt, ldqt, s, lds, cb);
     else
