@@ -275,11 +275,11 @@ def _dense_fprop_reference(mode):
 @pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
 def test_wgrad_224_column_tiles(hip, orc, out):
     """Per-column-scale GEMMs (Wgrad) in the FP32-scale FP8 mode on shapes
-    where 256 x 224 tiles fill the CUs better than 256 x 256 ones (on a
-    256-CU MI355X): dW[1000x2016] over 384 tokens (nine whole 224-column
-    tiles, ragged rows) and dW[520x2000] over 256 tokens (a last tile of 208
-    columns, a last row tile of 8 rows); every output compared."""
-    for i, (T, Nw, C) in enumerate([(384, 1000, 2016), (256, 520, 2000)]):
+    whose launch on a 256-CU MI355X takes 256 x 224 tiles (one round of 256
+    of them, against 224 wide tiles): dW[2000x7104] over 256 tokens (a last
+    row tile of 208 rows, a last column tile of 160 columns) and dW[1800x7168]
+    over 384 tokens (a last row tile of 8 rows); every output compared."""
+    for i, (T, Nw, C) in enumerate([(256, 2000, 7104), (384, 1800, 7168)]):
         dY = inputs.random_bf16(161 + 2 * i, (T, Nw), sd=1e-3)
         X = inputs.random_bf16(162 + 2 * i, (T, C))
         qdt, sdt, _, wqdt, wsdt, _ = quant_both(hip, orc, dY, "col", 0)
