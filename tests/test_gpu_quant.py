@@ -90,11 +90,14 @@ def _block_case(name):
         return workload("dense_fprop")["W"]
     if name == "expert_W":
         return workload("expert_backward")["W"]
+    if name == "odd_blocks":
+        # five block columns: the last workgroup of a block row holds one block
+        return inputs.random_bf16(9, (300, 640), sd=0.02)
     raise KeyError(name)
 
 
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp32", "pow2"])
-@pytest.mark.parametrize("case", ["tiny_W", "edges", "expert_W", "dense_W"])
+@pytest.mark.parametrize("case", ["tiny_W", "edges", "odd_blocks", "expert_W", "dense_W"])
 def test_quant_block(hip, orc, case, mode):
     w = _block_case(case)
     log(f"quant_block {case} {w.shape} mode={mode}")
