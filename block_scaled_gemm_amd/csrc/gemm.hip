@@ -23,8 +23,9 @@
 //  the matrix core's own limited accumulation inside the group.  Dense
 //  launches: workgroup tile 256 (m) x 256 (n), 8 waves of 64x128 (4x8
 //  sub-tiles of 16x16), the last partial round of tiles as 256 x 128 tiles
-//  (waves of 64x64); split-K and grouped launches: 256 x 128, and 128 x 128
-//  for a grouped row tile of at most 128 rows.
+//  (waves of 64x64); split-K launches: 256 x 128; grouped launches: 128
+//  columns by 64, 128, 192 or 256 rows, with loader and compute waves apart
+//  (grouped_split_kernel).
 //
 //  ACC_MFMA8_POW2 (2).  As ACC_MFMA8, for power-of-two scales: they enter
 //  the scaled MFMA as E8M0 block scales and every group is accumulated by
@@ -106,23 +107,6 @@ struct Shape<1> {
     static constexpr int STAGES = 2;
     __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<0>::wave_grid(wave, wm, wn); }
 };
-//  Shape 2: 128 x 128, waves of 64 x 32, three K groups in flight (four
-//    stages).  The grouped kernels' FP8 paths run row tiles of at most 128
-//    rows (a typical expert) with it: every wave computes, and the stage
-//    holds no rows past the expert, where the 256-row tile idles half its
-//    waves and stages twice the activation bytes.
-template <>
-struct Shape<2> {
-    static constexpr int BM = 128, BN = 128;
-    static constexpr int WM = 64, WN = 32;
-    static constexpr int STAGES = 4;
-    // SIMD s holds waves s and s + 4, one from each m-slot.
-    __device__ static void wave_grid(int wave, int& wm, int& wn) {
-        wm = wave >> 2;
-        wn = wave & 3;
-    }
-};
-
 //  Shape 5: 128 x 128 with waves of 32 x 64 and two stages (66 KB, which
 //    the 128 x 128 fp32 output image also fits): the K-grouped Wgrad, whose
 //    experts hold one or two K groups and whose cost is the fp32 output,
@@ -165,6 +149,39 @@ struct Shape<8> {
     __device__ static void wave_grid(int wave, int& wm, int& wn) { Shape<5>::wave_grid(wave, wm, wn); }
 };
 
+//  Shapes 10 and 11: the grouped GEMMs' FP8 paths with the roles apart --
+//    waves 0..3 only stage, waves 4..7 only compute, each of those owning
+//    32 columns of the 128-column tile and every row of the row tile.
+//    Shape 10 takes row tiles of 65..128 rows (four stages, three K groups
+//    in flight), shape 11 those of 193..256 rows (three stages).
+template <>
+struct Shape<10> {
+    static constexpr int BM = 128, BN = 128;
+    static constexpr int WM = 128, WN = 32;
+    static constexpr int STAGES = 4;
+};
+template <>
+struct Shape<11> {
+    static constexpr int BM = 256, BN = 128;
+    static constexpr int WM = 256, WN = 32;
+    static constexpr int STAGES = 3;
+};
+//  Shapes 12 and 13: the same for row tiles of 129..192 rows (three
+//    stages) and of at most 64 rows (four stages), so a tile stages and
+//    multiplies at most 63 rows past the expert's end.
+template <>
+struct Shape<12> {
+    static constexpr int BM = 192, BN = 128;
+    static constexpr int WM = 192, WN = 32;
+    static constexpr int STAGES = 3;
+};
+template <>
+struct Shape<13> {
+    static constexpr int BM = 64, BN = 128;
+    static constexpr int WM = 64, WN = 32;
+    static constexpr int STAGES = 4;
+};
+
 // LDS map of one stage: A codes [BM][128], B codes [BN][128], sa [BM],
 // B scales: per-column [BN] (tile kind) or the BN/128 block scalars.
 template <int SH>
@@ -198,6 +215,13 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// The same with the non-temporal hint: for operands that stream through
+// once (the grouped GEMMs' expert weights), so they do not displace the
+// activation rows that the other column tiles of the expert re-read from L2.
+__device__ __forceinline__ void dma16s_nt(uint32_t voff, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
 __device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t lds) {
@@ -269,7 +293,7 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
 // moves 8 rows of 128 B: lane i fetches chunk (i%8) ^ swz(row) of row i/8
 // and lands at LDS base + 16*i.  Only the LOADERS waves issue.
 
-template <int SH, int KIND>
+template <int SH, int KIND, bool NTB = false>
 struct Stager {
     static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     static constexpr int NA = BM / 8 / LOADERS, NB = BN / 8 / LOADERS;
@@ -315,8 +339,12 @@ struct Stager {
         for (int ins = 0; ins < NA; ins++)
             dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
 #pragma unroll
-        for (int ins = 0; ins < NB; ins++)
-            dma16s(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
+        for (int ins = 0; ins < NB; ins++) {
+            if (NTB)
+                dma16s_nt(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
+            else
+                dma16s(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
+        }
         // scales: loader w loads sa rows 64w..64w+63 and the B scales --
         // per-column floats 64w..64w+63 (tile kind) or, block kind (loader
         // 0), the group's BN/128 block scalars (lane l loads block column
@@ -1095,9 +1123,11 @@ __global__ __launch_bounds__(THREADS) void gemm_wide_kernel(GemmArgs p, int64_t 
     }
 }
 
-// Grouped: workgroup (expert e, n-tile) walks the expert's m-tiles.
+// Grouped, exact mode: workgroup (expert e, n-tile) walks the expert's
+// m-tiles.  (The FP8 modes run grouped_split_kernel below.)
 template <int ACC, int KIND, int OUT>
 __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t tiles_n) {
+    static_assert(ACC == 0, "the exact mode");
     __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<0>::BYTES];
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t e = wid / tiles_n;
@@ -1117,16 +1147,272 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
     T.sb = p.sb + e * p.sb_estride;
     T.sb_s0 = p.sb_s0;
     T.sb_s1 = p.sb_s1;
-    static_assert(Lds<2>::BYTES <= Lds<0>::BYTES, "both row-tile shapes fit the LDS");
     for (int64_t m0 = r0; m0 < r1; m0 += Shape<0>::BM) {
         T.m0 = m0;
-        if constexpr (ACC != 0) {
-            if (r1 - m0 <= Shape<2>::BM) {
-                run_tile<ACC, 2, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
-                continue;
+        run_tile<ACC, 0, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
+    }
+}
+
+// ==== grouped GEMMs with the roles apart ===================================================
+//
+// The FP8 paths of the grouped GEMMs stream every weight tile once and are
+// bound by that staging, not by the matrix cores.  Waves 0..3 only issue
+// the direct loads (the weight codes with the non-temporal hint) and waves
+// 4..7 only compute, so a loader's issue of the next groups never waits
+// behind its own MFMA and promotion work.  Compute wave c (on SIMD c) owns
+// columns 32c..32c+31: its two B fragments stay in registers while the A
+// fragments of the tile's valid 16-row blocks stream past them, so an
+// expert with few rows issues MFMAs for its own rows only.
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// The fragment of rows 16i + lane % 16 from per-lane LDS byte addresses of
+// the two chunks in row lane % 16 (rows 16 apart share the swizzle, so row
+// block i is at +2048 i, an immediate offset).
+__device__ __forceinline__ v8i f8_frag_at(uint32_t lo, uint32_t hi, int i) {
+    const u32x4_t x = *(lds_u4*)(uintptr_t)(lo + 2048 * i);
+    const u32x4_t y = *(lds_u4*)(uintptr_t)(hi + 2048 * i);
+    v8i r;
+    r[0] = (int)x.x; r[1] = (int)x.y; r[2] = (int)x.z; r[3] = (int)x.w;
+    r[4] = (int)y.x; r[5] = (int)y.y; r[6] = (int)y.z; r[7] = (int)y.w;
+    return r;
+}
+
+// `stage`: LDS byte address of the stage, opaque to the compiler.  The
+// stage offsets of the later stages do not fit a DS instruction's 16-bit
+// offset; folded into every read they made the compiler keep an address
+// register per row block and spill them.  From one per-lane base per
+// operand, every read of a step takes an immediate offset.
+template <int ACC, int SH, int KIND>
+__device__ __forceinline__ void compute_cols(uint32_t stage, int c, int lane, v4f (&acc)[Shape<SH>::BM / 16][2]) {
+    constexpr int MI = Shape<SH>::BM / 16;
+    static_assert(Shape<SH>::BN == 128, "one block column per tile");
+    const int nbase = 32 * c, c0 = 2 * (lane >> 4), l16 = lane & 15;
+    const uint32_t alo = stage + Lds<SH>::A + f8_off(l16, c0), ahi = stage + Lds<SH>::A + f8_off(l16, c0 + 1);
+    const uint32_t bb = stage + Lds<SH>::B + 128 * nbase;
+    const v8i b0 = f8_frag_at(bb + f8_off(l16, c0), bb + f8_off(l16, c0 + 1), 0);
+    const v8i b1 = f8_frag_at(bb + f8_off(l16, c0), bb + f8_off(l16, c0 + 1), 1);
+    lds_f32* sal = (lds_f32*)(uintptr_t)(stage + Lds<SH>::SA + 4 * l16);  // row scales, +16 per row block
+    lds_f32* sbl = (lds_f32*)(uintptr_t)(stage + Lds<SH>::SB);
+    struct {
+        lds_f32* sb;
+    } sp = {sbl};
+    // Every row block of the tile (rows past m_valid come from the stage's
+    // clamped rows and are never stored; a data-dependent exit made the
+    // compiler copy the accumulators at every exit and spill), in pairs,
+    // software-pipelined: the next pair's A fragments and scales are read
+    // from LDS before this pair's MFMAs, and the previous pair's partials
+    // are promoted while this pair's MFMAs run.
+    v8i a[2];
+    float sv[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        a[h] = f8_frag_at(alo, ahi, h);
+        sv[h] = sal[16 * h];
+    }
+    if constexpr (ACC == 2) {
+        const int s0 = e8m0(KIND == 0 ? sp.sb[0] : sp.sb[nbase + (lane & 15)]);
+        const int s1 = e8m0(KIND == 0 ? sp.sb[0] : sp.sb[nbase + 16 + (lane & 15)]);
+#pragma unroll
+        for (int i = 0; i < MI; i += 2) {
+            v8i na[2];
+            float ns[2];
+            if (i + 2 < MI) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    na[h] = f8_frag_at(alo, ahi, i + 2 + h);
+                    ns[h] = sal[16 * (i + 2 + h)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int sab = e8m0(sv[h]);
+                acc[i + h][0] =
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, a[h], acc[i + h][0], 0, 0, 0, s0, 0, sab);
+                acc[i + h][1] =
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, a[h], acc[i + h][1], 0, 0, 0, s1, 0, sab);
+            }
+            if (i + 2 < MI) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    a[h] = na[h];
+                    sv[h] = ns[h];
+                }
             }
         }
-        run_tile<ACC, 0, KIND, OUT>(T, 0, p.K / 128, p.d, p.ldd, smem);
+    } else {
+        const float sbk = KIND == 0 ? sp.sb[0] : 1.f;
+        v4f sbn0 = {1.f, 1.f, 1.f, 1.f}, sbn1 = sbn0;
+        if (KIND == 1) {
+            sbn0 = *(__attribute__((address_space(3))) const v4f*)(sp.sb + nbase + 4 * (lane >> 4));
+            sbn1 = *(__attribute__((address_space(3))) const v4f*)(sp.sb + nbase + 16 + 4 * (lane >> 4));
+        }
+        v4f pp[2][2];
+        float pc[2];
+        auto promote = [&](int i) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                if (KIND == 0) {
+                    acc[i + h][0] += pp[h][0] * pc[h];
+                    acc[i + h][1] += pp[h][1] * pc[h];
+                } else {
+                    acc[i + h][0] += (pp[h][0] * pc[h]) * sbn0;
+                    acc[i + h][1] += (pp[h][1] * pc[h]) * sbn1;
+                }
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < MI; i += 2) {
+            v8i na[2];
+            float ns[2];
+            if (i + 2 < MI) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    na[h] = f8_frag_at(alo, ahi, i + 2 + h);
+                    ns[h] = sal[16 * (i + 2 + h)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            v4f p[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                p[h][0] = mfma8_group(b0, a[h]);
+                p[h][1] = mfma8_group(b1, a[h]);
+            }
+            if (i > 0) promote(i - 2);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                pp[h][0] = p[h][0];
+                pp[h][1] = p[h][1];
+                pc[h] = KIND == 0 ? sv[h] * sbk : sv[h];
+            }
+            if (i + 2 < MI) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    a[h] = na[h];
+                    sv[h] = ns[h];
+                }
+            }
+        }
+        promote(MI - 2);
+    }
+}
+
+template <int ACC, int SH, int KIND, int OUT>
+__device__ __forceinline__ void run_tile_split(const Tile& T, int64_t g1, void* d, int64_t ldd, uint8_t* smem) {
+    static_assert(ACC != 0 && OUT <= 1, "FP8 paths, bf16 or fp32 output");
+    constexpr int S = Shape<SH>::STAGES, MI = Shape<SH>::BM / 16;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    float* ep = (float*)smem;
+
+    // The two roles run separate loops that meet at the same barriers (one
+    // per group and one after the last): s_barrier waits for every wave of
+    // the workgroup whichever barrier instruction each one is at.  Kept
+    // apart, the compute loop's accumulators never merge with a path that
+    // leaves them untouched (such merges cost a copy of every accumulator).
+    if (wave < LOADERS) {
+        Stager<SH, KIND, true> stg;
+        stg.init(T, wave, lane);
+#pragma unroll
+        for (int s = 0; s < S - 1; s++)
+            if (s < g1) stg.issue(T, s, smem, s * Lds<SH>::STAGE, wave);
+        // as in run_tile: wait until group g has landed (the S - 2 following
+        // groups may still be in flight), meet the compute waves at the
+        // barrier, refill the stage of group g - 1
+        constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / LOADERS;
+        static_assert((S == 4 || S == 3) && (S - 2) * PER <= 63, "wait counts cover this pipeline");
+        auto step = [&](auto ss, int64_t g) {
+            constexpr int SS = decltype(ss)::value;
+            if (S == 4 && g + 2 < g1)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * PER) : "memory");
+            else if (S >= 3 && g + 1 < g1)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            if (g + S - 1 < g1) stg.issue(T, g + S - 1, smem, ((SS + S - 1) % S) * Lds<SH>::STAGE, wave);
+        };
+        for (int64_t g = 0; g < g1; g += S) {
+            step(std::integral_constant<int, 0>(), g);
+            if (g + 1 < g1) step(std::integral_constant<int, 1>(), g + 1);
+            if (g + 2 < g1) step(std::integral_constant<int, 2>(), g + 2);
+            if constexpr (S == 4)
+                if (g + 3 < g1) step(std::integral_constant<int, 3>(), g + 3);
+        }
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // every group used
+    } else {
+        const int c = wave - LOADERS;
+        v4f acc[MI][2];
+#pragma unroll
+        for (int i = 0; i < MI; i++) acc[i][0] = acc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+        auto step = [&](auto ss) {
+            constexpr int SS = decltype(ss)::value;
+            asm volatile("s_barrier" ::: "memory");
+            uint32_t stage = lds_addr(smem) + SS * Lds<SH>::STAGE;
+            asm volatile("" : "+s"(stage));
+            compute_cols<ACC, SH, KIND>(stage, c, lane, acc);
+        };
+        for (int64_t g = 0; g < g1; g += S) {
+            step(std::integral_constant<int, 0>());
+            if (g + 1 < g1) step(std::integral_constant<int, 1>());
+            if (g + 2 < g1) step(std::integral_constant<int, 2>());
+            if constexpr (S == 4)
+                if (g + 3 < g1) step(std::integral_constant<int, 3>());
+        }
+        asm volatile("s_barrier" ::: "memory");  // the stages hold the output image next
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                put4<SH>(ep, 16 * i + (lane & 15), 32 * c + 16 * j + 4 * (lane >> 4), acc[i][j][0], acc[i][j][1],
+                         acc[i][j][2], acc[i][j][3]);
+    }
+    __syncthreads();
+    write_tile_image<SH, OUT, true>(ep, T, T.n0, d, ldd);
+    __syncthreads();  // a following row tile refills the stages
+}
+
+// Grouped, FP8 paths: workgroup (expert e, n-tile) walks the expert's rows
+// in 256-row tiles, a last tile of fewer rows on the smallest shape that
+// holds them.
+template <int ACC, int KIND, int OUT>
+__global__ __launch_bounds__(THREADS) void grouped_split_kernel(GemmArgs p, int64_t tiles_n) {
+    constexpr int LDS_BYTES = Lds<11>::BYTES;
+    static_assert(Lds<10>::BYTES <= LDS_BYTES && Lds<12>::BYTES <= LDS_BYTES && Lds<13>::BYTES <= LDS_BYTES,
+                  "every row-tile shape fits");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t e = wid / tiles_n;
+    const int64_t tn = wid % tiles_n;
+    const int64_t r0 = p.offsets[e], r1 = p.offsets[e + 1];
+
+    Tile T;
+    T.m_end = r1;
+    T.n0 = tn * 128;
+    T.n_end = p.N;
+    T.a = p.a;
+    T.lda = p.lda;
+    T.sa = p.sa;
+    T.ldsa = p.ldsa;
+    T.b = p.b + e * p.b_estride;
+    T.ldb = p.ldb;
+    T.sb = p.sb + e * p.sb_estride;
+    T.sb_s0 = p.sb_s0;
+    T.sb_s1 = p.sb_s1;
+    for (int64_t m0 = r0; m0 < r1; m0 += Shape<11>::BM) {
+        T.m0 = m0;
+        const int64_t rows = r1 - m0;
+        if (rows <= Shape<13>::BM)
+            run_tile_split<ACC, 13, KIND, OUT>(T, p.K / 128, p.d, p.ldd, smem);
+        else if (rows <= Shape<10>::BM)
+            run_tile_split<ACC, 10, KIND, OUT>(T, p.K / 128, p.d, p.ldd, smem);
+        else if (rows <= Shape<12>::BM)
+            run_tile_split<ACC, 12, KIND, OUT>(T, p.K / 128, p.d, p.ldd, smem);
+        else
+            run_tile_split<ACC, 11, KIND, OUT>(T, p.K / 128, p.d, p.ldd, smem);
     }
 }
 
@@ -1465,18 +1751,34 @@ template <int ACC>
 static hipError_t launch_grouped_acc(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_n = (g.N + Shape<0>::BN - 1) / Shape<0>::BN;
     const dim3 grid((unsigned)(tiles_n * g.G));
-    if (g.bscale_kind == 0) {
-        if (g.out_f32)
-            hipLaunchKernelGGL((grouped_kernel<ACC, 0, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
-        else
-            hipLaunchKernelGGL((grouped_kernel<ACC, 0, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
-    } else {
-        if (g.out_f32)
-            hipLaunchKernelGGL((grouped_kernel<ACC, 1, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
-        else
-            hipLaunchKernelGGL((grouped_kernel<ACC, 1, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+    if constexpr (ACC != 0) {
+        if (g.bscale_kind == 0) {
+            if (g.out_f32)
+                hipLaunchKernelGGL((grouped_split_kernel<ACC, 0, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+            else
+                hipLaunchKernelGGL((grouped_split_kernel<ACC, 0, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        } else {
+            if (g.out_f32)
+                hipLaunchKernelGGL((grouped_split_kernel<ACC, 1, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+            else
+                hipLaunchKernelGGL((grouped_split_kernel<ACC, 1, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    else {
+        if (g.bscale_kind == 0) {
+            if (g.out_f32)
+                hipLaunchKernelGGL((grouped_kernel<ACC, 0, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+            else
+                hipLaunchKernelGGL((grouped_kernel<ACC, 0, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        } else {
+            if (g.out_f32)
+                hipLaunchKernelGGL((grouped_kernel<ACC, 1, 1>), grid, dim3(THREADS), 0, st, g, tiles_n);
+            else
+                hipLaunchKernelGGL((grouped_kernel<ACC, 1, 0>), grid, dim3(THREADS), 0, st, g, tiles_n);
+        }
+        return hipGetLastError();
+    }
 }
 
 template <int ACC>
