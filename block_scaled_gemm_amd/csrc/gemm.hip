@@ -239,6 +239,20 @@ __device__ __forceinline__ void wait_and_barrier(int wave) {
         asm volatile("s_barrier" ::: "memory");
 }
 
+// Loader wave: wait until at most n (wave-uniform, 0 <= n <= N) of its
+// direct loads are in flight, then the barrier.  s_waitcnt takes its count
+// as an immediate, so n selects one of the N + 1 forms.
+template <int N>
+__device__ __forceinline__ void wait_n_and_barrier(int n) {
+    if constexpr (N > 0) {
+        if (n < N) {
+            wait_n_and_barrier<N - 1>(n);
+            return;
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Chunk swizzle of a tile row: (row mod 8) ^ bit 3 of the row.  The 16
 // rows of a fragment read (16 lanes per LDS cycle, 256 B over the banks)
 // fall 8 on even and 8 on odd bank halves, and each half sees 8 distinct
@@ -301,8 +315,20 @@ struct Stager {
     static_assert(SA_INS <= LOADERS && SB_INS <= LOADERS, "one instruction per loader for each scale");
     static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
     uint32_t va[NA], vb[NB], vsa, vsb;
+    // NTB (the grouped kernels): this loader issues only the A instructions
+    // whose 8-row block holds a row of the tile, na_valid of them per group
+    // (wave-uniform); the compute waves' rows past the end then read stale
+    // LDS and are never stored.  Otherwise every instruction is issued.
+    int na_valid;
 
     __device__ __forceinline__ void init(const Tile& T, int wave, int lane) {
+        {
+            const int64_t rows = T.m_end - T.m0;
+            // blocks ins * LOADERS + wave below ceil(rows / 8)
+            const int64_t blocks = (rows + 7) >> 3;
+            const int64_t n = blocks > wave ? (blocks - wave + LOADERS - 1) / LOADERS : 0;
+            na_valid = NTB ? (int)(n < NA ? n : NA) : NA;
+        }
 #pragma unroll
         for (int ins = 0; ins < NA; ins++) {
             const int row = (ins * LOADERS + wave) * 8 + (lane >> 3);
@@ -337,7 +363,7 @@ struct Stager {
         const uint32_t base = lds_addr(smem + stage);
 #pragma unroll
         for (int ins = 0; ins < NA; ins++)
-            dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
+            if (!NTB || ins < na_valid) dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
 #pragma unroll
         for (int ins = 0; ins < NB; ins++) {
             if (NTB)
@@ -1322,15 +1348,19 @@ __device__ __forceinline__ void run_tile_split(const Tile& T, int64_t g1, void* 
             if (s < g1) stg.issue(T, s, smem, s * Lds<SH>::STAGE, wave);
         // as in run_tile: wait until group g has landed (the S - 2 following
         // groups may still be in flight), meet the compute waves at the
-        // barrier, refill the stage of group g - 1
+        // barrier, refill the stage of group g - 1.  This loader's tile
+        // loads per group: its valid A instructions and its B ones; its
+        // scale loads come on top, so waiting for k * per outstanding is
+        // conservative.
         constexpr int PER = (Shape<SH>::BM + Shape<SH>::BN) / 8 / LOADERS;
         static_assert((S == 4 || S == 3) && (S - 2) * PER <= 63, "wait counts cover this pipeline");
+        const int per = stg.na_valid + Stager<SH, KIND, true>::NB;
         auto step = [&](auto ss, int64_t g) {
             constexpr int SS = decltype(ss)::value;
             if (S == 4 && g + 2 < g1)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * PER) : "memory");
+                wait_n_and_barrier<2 * PER>(2 * per);
             else if (S >= 3 && g + 1 < g1)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+                wait_n_and_barrier<PER>(per);
             else
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             if (g + S - 1 < g1) stg.issue(T, g + S - 1, smem, ((SS + S - 1) % S) * Lds<SH>::STAGE, wave);
