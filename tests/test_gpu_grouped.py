@@ -69,6 +69,66 @@ def test_grouped_short_k(hip, orc, K, accum):
     check(out_f64(y), r, rabs, 1, accum, K // 128, f"short K={K} accum={accum}")
 
 
+@pytest.mark.parametrize("accum", [1, 2], ids=["mfma8", "mfma8pow2"])
+@pytest.mark.parametrize("out", [1, 0], ids=["f32", "bf16"])
+def test_grouped_row_tile_boundaries(hip, orc, out, accum):
+    """Experts on each side of every row-tile size the FP8 kernels choose
+    (64, 128, 192, 256 rows), none, a few, and more than one 256-row tile
+    (300 and 520 rows: a last tile of 44 and of 8 rows), N = 384, K = 640
+    (five K groups: the three- and four-stage pipelines' tails), every
+    output against the oracle."""
+    counts = [64, 65, 128, 129, 192, 193, 256, 0, 7, 520, 300]
+    offsets = np.zeros(len(counts) + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    Xcat = inputs.random_bf16(207, (int(offsets[-1]), 640))
+    W = inputs.random_bf16(208, (len(counts), 384, 640), sd=0.02, outliers=False)
+    qx, sx, qw, sw, wqx, wsx, wqw, wsw = quant_experts(hip, orc, Xcat, W, 1)
+    y = hip.fp8_grouped_gemm(dev(offsets), qx, sx, qw, sw, out, accum=accum)
+    r = orc.grouped_gemm(offsets, wqx, wsx, wqw, wsw)
+    rabs = orc.grouped_gemm_abs(offsets, wqx, wsx, wqw, wsw)
+    for e in range(len(counts)):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            check(out_f64(y)[r0:r1], r[r0:r1], rabs[r0:r1], out, accum, 5,
+                  f"expert {e} ({counts[e]} rows) out={out} accum={accum}")
+
+
+@ACCUMS_POW2
+def test_grouped_strided_column_scales(hip, orc, accum):
+    """The strided grouped GEMM with per-column B scales (tile kind): each
+    expert's B[N x K] quantised in 1x128 groups along K, scales [K/128][N];
+    experts of 0, 70, 200 and 300 rows, N = 256, K = 384, power-of-two
+    scales, fp32 out, every output against the oracle."""
+    counts = [0, 70, 200, 300]
+    G, N, K = len(counts), 256, 384
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    Xcat = inputs.random_bf16(209, (int(offsets[-1]), K))
+    Bw = inputs.random_bf16(210, (G * N, K), sd=0.02, outliers=False)
+    qx, sx = hip.fp8_quant_tile(dev_bf16(Xcat), hip.AXIS_ROW, 1)
+    wqx, wsx = orc.quant_tile(Xcat, 0, 1)
+    qb = torch.empty((G * N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, K // 128, N), dtype=torch.float32, device="cuda")
+    wq, ws = [], []
+    for e in range(G):
+        hip.fp8_quant_tile(dev_bf16(Bw[e * N:(e + 1) * N]), hip.AXIS_ROW, 1, q=qb[e * N:(e + 1) * N], s=sb[e])
+        q_e, s_e = orc.quant_tile(Bw[e * N:(e + 1) * N], 0, 1)
+        np.testing.assert_array_equal(host(qb[e * N:(e + 1) * N]), q_e)
+        wq.append(q_e)
+        ws.append(s_e)
+    y = hip.fp8_grouped_gemm_strided(dev(offsets), qx, sx, G, N, qb, K, N * K, sb, hip.BSCALE_TILE, N, 0,
+                                     (K // 128) * N, 1, accum=accum)
+    got = out_f64(y)
+    for e in range(G):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        a, sa = wqx[r0:r1], np.ascontiguousarray(wsx[:, r0:r1])
+        r = orc.gemm(a, sa, wq[e], ws[e], 1, N, 0)
+        rabs = orc.gemm_abs(a, sa, wq[e], ws[e], 1, N, 0)
+        check(got[r0:r1], r, rabs, 1, accum, K // 128, f"strided tile-kind expert {e} accum={accum}")
+
+
 @pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
 def test_grouped_rows_beyond_offsets_untouched(hip, orc, accum):
     """Rows past offsets[G] (rows_bound larger than the routed rows) are not
