@@ -1187,8 +1187,9 @@ __global__ __launch_bounds__(THREADS) void grouped_kernel(GemmArgs p, int64_t ti
 // 4..7 only compute, so a loader's issue of the next groups never waits
 // behind its own MFMA and promotion work.  Compute wave c (on SIMD c) owns
 // columns 32c..32c+31: its two B fragments stay in registers while the A
-// fragments of the tile's valid 16-row blocks stream past them, so an
-// expert with few rows issues MFMAs for its own rows only.
+// fragments of the tile's 16-row blocks stream past them.  A row tile is
+// the smallest of 64, 128, 192 or 256 rows that holds the expert's
+// remaining rows, so an expert with few rows stages and multiplies few.
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
@@ -1221,10 +1222,7 @@ __device__ __forceinline__ void compute_cols(uint32_t stage, int c, int lane, v4
     const v8i b0 = f8_frag_at(bb + f8_off(l16, c0), bb + f8_off(l16, c0 + 1), 0);
     const v8i b1 = f8_frag_at(bb + f8_off(l16, c0), bb + f8_off(l16, c0 + 1), 1);
     lds_f32* sal = (lds_f32*)(uintptr_t)(stage + Lds<SH>::SA + 4 * l16);  // row scales, +16 per row block
-    lds_f32* sbl = (lds_f32*)(uintptr_t)(stage + Lds<SH>::SB);
-    struct {
-        lds_f32* sb;
-    } sp = {sbl};
+    lds_f32* sb = (lds_f32*)(uintptr_t)(stage + Lds<SH>::SB);  // block scalar, or per-column scales
     // Every row block of the tile (rows past m_valid come from the stage's
     // clamped rows and are never stored; a data-dependent exit made the
     // compiler copy the accumulators at every exit and spill), in pairs,
@@ -1239,8 +1237,8 @@ __device__ __forceinline__ void compute_cols(uint32_t stage, int c, int lane, v4
         sv[h] = sal[16 * h];
     }
     if constexpr (ACC == 2) {
-        const int s0 = e8m0(KIND == 0 ? sp.sb[0] : sp.sb[nbase + (lane & 15)]);
-        const int s1 = e8m0(KIND == 0 ? sp.sb[0] : sp.sb[nbase + 16 + (lane & 15)]);
+        const int s0 = e8m0(KIND == 0 ? sb[0] : sb[nbase + (lane & 15)]);
+        const int s1 = e8m0(KIND == 0 ? sb[0] : sb[nbase + 16 + (lane & 15)]);
 #pragma unroll
         for (int i = 0; i < MI; i += 2) {
             v8i na[2];
@@ -1270,11 +1268,11 @@ __device__ __forceinline__ void compute_cols(uint32_t stage, int c, int lane, v4
             }
         }
     } else {
-        const float sbk = KIND == 0 ? sp.sb[0] : 1.f;
+        const float sbk = KIND == 0 ? sb[0] : 1.f;
         v4f sbn0 = {1.f, 1.f, 1.f, 1.f}, sbn1 = sbn0;
         if (KIND == 1) {
-            sbn0 = *(__attribute__((address_space(3))) const v4f*)(sp.sb + nbase + 4 * (lane >> 4));
-            sbn1 = *(__attribute__((address_space(3))) const v4f*)(sp.sb + nbase + 16 + 4 * (lane >> 4));
+            sbn0 = *(__attribute__((address_space(3))) const v4f*)(sb + nbase + 4 * (lane >> 4));
+            sbn1 = *(__attribute__((address_space(3))) const v4f*)(sb + nbase + 16 + 4 * (lane >> 4));
         }
         v4f pp[2][2];
         float pc[2];
