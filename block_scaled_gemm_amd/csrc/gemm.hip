@@ -307,7 +307,10 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t 
 // moves 8 rows of 128 B: lane i fetches chunk (i%8) ^ swz(row) of row i/8
 // and lands at LDS base + 16*i.  Only the LOADERS waves issue.
 
-template <int SH, int KIND, bool NTB = false>
+// GROUPED: the grouped kernels' form -- the weight codes are loaded with
+// the non-temporal hint, and a loader issues only the A instructions whose
+// 8-row block holds a row of the tile (see na_valid).
+template <int SH, int KIND, bool GROUPED = false>
 struct Stager {
     static constexpr int BM = Shape<SH>::BM, BN = Shape<SH>::BN;
     static constexpr int NA = BM / 8 / LOADERS, NB = BN / 8 / LOADERS;
@@ -315,10 +318,10 @@ struct Stager {
     static_assert(SA_INS <= LOADERS && SB_INS <= LOADERS, "one instruction per loader for each scale");
     static_assert(KIND == 1 || BN <= 64 * 128, "block scalars of one tile fit one instruction");
     uint32_t va[NA], vb[NB], vsa, vsb;
-    // NTB (the grouped kernels): this loader issues only the A instructions
-    // whose 8-row block holds a row of the tile, na_valid of them per group
-    // (wave-uniform); the compute waves' rows past the end then read stale
-    // LDS and are never stored.  Otherwise every instruction is issued.
+    // GROUPED: this loader issues only the A instructions whose 8-row block
+    // holds a row of the tile, na_valid of them per group (wave-uniform);
+    // the compute waves' rows past the end then read stale LDS and are never
+    // stored.  Otherwise every instruction is issued.
     int na_valid;
 
     __device__ __forceinline__ void init(const Tile& T, int wave, int lane) {
@@ -327,7 +330,7 @@ struct Stager {
             // blocks ins * LOADERS + wave below ceil(rows / 8)
             const int64_t blocks = (rows + 7) >> 3;
             const int64_t n = blocks > wave ? (blocks - wave + LOADERS - 1) / LOADERS : 0;
-            na_valid = NTB ? (int)(n < NA ? n : NA) : NA;
+            na_valid = GROUPED ? (int)(n < NA ? n : NA) : NA;
         }
 #pragma unroll
         for (int ins = 0; ins < NA; ins++) {
@@ -363,10 +366,10 @@ struct Stager {
         const uint32_t base = lds_addr(smem + stage);
 #pragma unroll
         for (int ins = 0; ins < NA; ins++)
-            if (!NTB || ins < na_valid) dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
+            if (!GROUPED || ins < na_valid) dma16s(va[ins], a, base + Lds<SH>::A + (ins * LOADERS + wave) * 8 * 128);
 #pragma unroll
         for (int ins = 0; ins < NB; ins++) {
-            if (NTB)
+            if (GROUPED)
                 dma16s_nt(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
             else
                 dma16s(vb[ins], b, base + Lds<SH>::B + (ins * LOADERS + wave) * 8 * 128);
