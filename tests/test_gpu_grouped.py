@@ -129,6 +129,26 @@ def test_grouped_strided_column_scales(hip, orc, accum):
         check(got[r0:r1], r, rabs, 1, accum, K // 128, f"strided tile-kind expert {e} accum={accum}")
 
 
+@ACCUMS_POW2
+def test_grouped_empty_k(hip, orc, accum):
+    """K = 0: every routed row's output is the empty sum, zero, in every
+    row-tile shape (experts of 70, 0, 300 and 150 rows); rows past
+    offsets[G] keep their contents."""
+    counts = [70, 0, 300, 150]
+    G, N = len(counts), 256
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    rows = int(offsets[-1])
+    a = torch.zeros((rows + 10, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((1, rows + 10), dtype=torch.float32, device="cuda")
+    b = torch.zeros((G, N, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((G, N // 128, 1), dtype=torch.float32, device="cuda")
+    d = torch.full((rows + 10, N), 7.0, dtype=torch.float32, device="cuda")
+    hip.fp8_grouped_gemm(dev(offsets), a, sa, b, sb, 1, rows_bound=rows + 10, d=d, accum=accum)
+    assert torch.count_nonzero(d[:rows]).item() == 0
+    assert torch.all(d[rows:] == 7.0).item()
+
+
 @pytest.mark.parametrize("accum", [0, 1], ids=["acc32", "mfma8"])
 def test_grouped_rows_beyond_offsets_untouched(hip, orc, accum):
     """Rows past offsets[G] (rows_bound larger than the routed rows) are not
